@@ -1,0 +1,219 @@
+"""CPU oracle for row-scaled NVFP4 quantize-transpose -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product path (the HIP library and
+its Python binding) never imports it, and it imports nothing from the
+product. It wraps the scalar C implementation in ``nvfp4_oracle.c`` (every
+floating-point step one IEEE binary32 operation, see that file for the
+definitions and the page passages they follow) with numpy arrays.
+
+Modes of the second-level amax (same numbering as the C file):
+  TENSOR   -- one amax for the whole tensor (per-tensor NVFP4)
+  LINE     -- one amax per line (row-scaled: per row, or per column for the
+              transposed copy)
+  ROWGROUP -- block b of a line uses amax[16*b] (per-group amax expanded along
+              the rows, used for the transposed copy of grouped tokens)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import build_oracle, library_path
+
+MODE_TENSOR = 0
+MODE_LINE = 1
+MODE_ROWGROUP = 2
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        build_oracle()
+    lib = ctypes.CDLL(path)
+    f32p = ctypes.POINTER(ctypes.c_float)
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    i64 = ctypes.c_int64
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    c_int = ctypes.c_int
+    c_f = ctypes.c_float
+    sigs = {
+        "orc_e2m1_value": (c_f, [c_int]),
+        "orc_e2m1_encode": (ctypes.c_uint8, [c_f]),
+        "orc_e4m3_value": (c_f, [c_int]),
+        "orc_e4m3_encode": (ctypes.c_uint8, [c_f]),
+        "orc_factor": (c_f, [c_f]),
+        "orc_factor_inv": (c_f, [c_f]),
+        "orc_global_encode_scale": (c_f, [c_f, c_f]),
+        "orc_quantize_line": (None, [f32p, i64, i64, f32p, c_f, u8p, u8p]),
+        "orc_quantize_rowwise": (None, [f32p, i64, i64, c_int, f32p, c_f, u8p, u8p]),
+        "orc_quantize_colwise": (None, [f32p, i64, i64, c_int, f32p, c_f, u8p, u8p]),
+        "orc_dequantize": (None, [u8p, u8p, i64, i64, c_int, f32p, c_f, f32p]),
+        "orc_amax_rows": (None, [f32p, i64, i64, f32p]),
+        "orc_amax_cols": (None, [f32p, i64, i64, f32p]),
+        "orc_amax_tensor": (c_f, [f32p, i64]),
+        "orc_group_amax_expand": (None, [f32p, i64p, i64, f32p]),
+        "orc_e2m1_encode_array": (None, [f32p, i64, u8p]),
+        "orc_e4m3_encode_array": (None, [f32p, i64, u8p]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if not np.isfinite(a).all():
+        raise ValueError("oracle inputs must be finite (NaN/inf are outside the contract)")
+    return a
+
+
+def _p(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# --------------------------------------------------------------------------- formats
+def e2m1_value(code: int) -> float:
+    return float(_load().orc_e2m1_value(int(code)))
+
+
+def e4m3_value(byte: int) -> float:
+    return float(_load().orc_e4m3_value(int(byte)))
+
+
+def e2m1_encode(v) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    if np.isnan(v).any():
+        raise ValueError("NaN is outside the contract")
+    out = np.empty(v.shape, dtype=np.uint8)
+    _load().orc_e2m1_encode_array(_p(v, ctypes.c_float), v.size, _p(out, ctypes.c_uint8))
+    return out
+
+
+def e4m3_encode(s) -> np.ndarray:
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    if np.isnan(s).any() or (s < 0).any():
+        raise ValueError("scales are non-negative and not NaN")
+    out = np.empty(s.shape, dtype=np.uint8)
+    _load().orc_e4m3_encode_array(_p(s, ctypes.c_float), s.size, _p(out, ctypes.c_uint8))
+    return out
+
+
+def factor_inv(bound: float) -> float:
+    return float(_load().orc_factor_inv(float(bound)))
+
+
+def global_encode_scale(a: float, bound: float) -> float:
+    return float(_load().orc_global_encode_scale(float(a), float(bound)))
+
+
+# --------------------------------------------------------------------------- amax
+def amax_rows(X) -> np.ndarray:
+    X = _f32(X)
+    M, K = X.shape
+    out = np.empty(M, dtype=np.float32)
+    _load().orc_amax_rows(_p(X, ctypes.c_float), M, K, _p(out, ctypes.c_float))
+    return out
+
+
+def amax_cols(X) -> np.ndarray:
+    X = _f32(X)
+    M, K = X.shape
+    out = np.empty(K, dtype=np.float32)
+    _load().orc_amax_cols(_p(X, ctypes.c_float), M, K, _p(out, ctypes.c_float))
+    return out
+
+
+def amax_tensor(X) -> np.float32:
+    X = _f32(X)
+    return np.float32(_load().orc_amax_tensor(_p(X, ctypes.c_float), X.size))
+
+
+def group_amax_expand(row_amax, group_end) -> np.ndarray:
+    ra = np.ascontiguousarray(row_amax, dtype=np.float32)
+    ge = np.ascontiguousarray(group_end, dtype=np.int64)
+    if ge.size and (ge[-1] != ra.size or (np.diff(ge) < 0).any() or ge[0] < 0):
+        raise ValueError("group_end must be non-decreasing and end at the row count")
+    out = np.zeros_like(ra)
+    _load().orc_group_amax_expand(_p(ra, ctypes.c_float), _p(ge, ctypes.c_int64), ge.size,
+                                  _p(out, ctypes.c_float))
+    return out
+
+
+# --------------------------------------------------------------------------- quantize
+def _amax_arg(mode: int, amax, n_lines: int, line_len: int) -> np.ndarray:
+    a = np.ascontiguousarray(np.atleast_1d(np.asarray(amax, dtype=np.float32)))
+    need = {MODE_TENSOR: 1, MODE_LINE: n_lines, MODE_ROWGROUP: line_len}[mode]
+    if a.size != need:
+        raise ValueError(f"amax for mode {mode} needs {need} entries, got {a.size}")
+    return a
+
+
+def quantize_rowwise(X, mode: int, amax, bound: float = 448.0):
+    """Row i of X -> (codes [M][ceil(K/2)] u8, scales [M][ceil(K/16)] u8)."""
+    X = _f32(X)
+    M, K = X.shape
+    a = _amax_arg(mode, amax, M, K)
+    q = np.zeros((M, (K + 1) // 2), dtype=np.uint8)
+    s = np.zeros((M, (K + 15) // 16), dtype=np.uint8)
+    _load().orc_quantize_rowwise(_p(X, ctypes.c_float), M, K, mode, _p(a, ctypes.c_float),
+                                 float(bound), _p(q, ctypes.c_uint8), _p(s, ctypes.c_uint8))
+    return q, s
+
+
+def quantize_colwise(X, mode: int, amax, bound: float = 448.0):
+    """Column j of X -> (codes [K][ceil(M/2)] u8, scales [K][ceil(M/16)] u8)."""
+    X = _f32(X)
+    M, K = X.shape
+    a = _amax_arg(mode, amax, K, M)
+    q = np.zeros((K, (M + 1) // 2), dtype=np.uint8)
+    s = np.zeros((K, (M + 15) // 16), dtype=np.uint8)
+    _load().orc_quantize_colwise(_p(X, ctypes.c_float), M, K, mode, _p(a, ctypes.c_float),
+                                 float(bound), _p(q, ctypes.c_uint8), _p(s, ctypes.c_uint8))
+    return q, s
+
+
+def quantize_line(x, block_amax, bound: float = 448.0):
+    """One line with an explicit second-level amax per 16-element block."""
+    x = _f32(x).ravel()
+    n = x.size
+    ba = np.ascontiguousarray(block_amax, dtype=np.float32).ravel()
+    if ba.size != (n + 15) // 16:
+        raise ValueError("one amax per block is required")
+    q = np.zeros((n + 1) // 2, dtype=np.uint8)
+    s = np.zeros((n + 15) // 16, dtype=np.uint8)
+    _load().orc_quantize_line(_p(x, ctypes.c_float), n, 1, _p(ba, ctypes.c_float), float(bound),
+                              _p(q, ctypes.c_uint8), _p(s, ctypes.c_uint8))
+    return q, s
+
+
+def dequantize(q, s, R: int, C: int, mode: int, amax, bound: float = 448.0) -> np.ndarray:
+    """Codes [R][ceil(C/2)] + scales [R][ceil(C/16)] -> FP32 [R][C]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    if q.size != R * ((C + 1) // 2) or s.size != R * ((C + 15) // 16):
+        raise ValueError("code/scale buffer sizes do not match R x C")
+    a = _amax_arg(mode, amax, R, C)
+    y = np.empty((R, C), dtype=np.float32)
+    _load().orc_dequantize(_p(q, ctypes.c_uint8), _p(s, ctypes.c_uint8), R, C, mode,
+                           _p(a, ctypes.c_float), float(bound), _p(y, ctypes.c_float))
+    return y
+
+
+def to_bf16_bits(y: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even FP32 -> BF16 (as uint16 bit patterns), by torch's
+    conversion (a library routine standing in for the rounding step)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)

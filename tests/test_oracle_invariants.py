@@ -1,0 +1,231 @@
+"""Invariants and closed forms that pin the oracle beyond its own code.
+
+Each test states a property that follows from the pages or from the
+mathematics of the format, and would fail for a plausible slip in the oracle
+(a dropped factor, a swapped operand, a wrong index or direction).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from precision_quantization_row_amd import workloads
+
+BOUNDS = (448.0, 256.0)
+
+
+def _f32(t: torch.Tensor) -> np.ndarray:
+    return t.float().numpy()
+
+
+def _unpack_codes(q: np.ndarray, n: int) -> np.ndarray:
+    lo = q & 0xF
+    hi = q >> 4
+    out = np.empty(q.shape[:-1] + (q.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out[..., :n]
+
+
+def _random_matrix(M, K, seed=0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x *= (10.0 ** rng.uniform(-3, 3, size=(M, 1))).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+
+
+# ----------------------------------------------------------------------------- amax
+def test_amax_closed_form():
+    x = _random_matrix(67, 93, seed=1)
+    x[3, :] = -0.0
+    x[5, 7] = -1e-40  # subnormal, negative
+    x[:, 11] = 0.0
+    assert np.array_equal(oracle.amax_rows(x), np.abs(x).max(axis=1))
+    assert np.array_equal(oracle.amax_cols(x), np.abs(x).max(axis=0))
+    assert oracle.amax_tensor(x) == np.abs(x).max()
+    # |-0| = +0: the amax bit pattern of an all -0 row is +0
+    assert oracle.amax_rows(x).view(np.uint32)[3] == 0
+
+
+def test_group_amax_expand_closed_form():
+    ra = np.array([1, 5, 2, 0, 0, 7, 3, 3], dtype=np.float32)
+    out = oracle.group_amax_expand(ra, [3, 3, 5, 8])
+    assert out.tolist() == [5, 5, 5, 0, 0, 7, 7, 7]
+
+
+# ------------------------------------------------------------------ transposition
+@pytest.mark.parametrize("shape", [(64, 48), (37, 53), (16, 1), (1, 33)])
+def test_columnwise_is_rowwise_of_transpose(shape):
+    M, K = shape
+    x = _random_matrix(M, K, seed=M * 100 + K)
+    ca = oracle.amax_cols(x)
+    for bound in BOUNDS:
+        qc, sc = oracle.quantize_colwise(x, oracle.MODE_LINE, ca, bound)
+        qt, st = oracle.quantize_rowwise(np.ascontiguousarray(x.T), oracle.MODE_LINE, ca, bound)
+        assert np.array_equal(qc, qt) and np.array_equal(sc, st)
+
+
+# ------------------------------------------------- row-scaled == per-tensor (scalar)
+def test_row_scaled_with_equal_amaxes_is_per_tensor():
+    n = 48
+    x = _random_matrix(n, n, seed=3)
+    x = np.clip(x, -1.0, 1.0)
+    np.fill_diagonal(x, 8.0)  # every row and every column has amax 8
+    x[np.arange(n), np.arange(n)[::-1]] = -8.0
+    ra, ca, ta = oracle.amax_rows(x), oracle.amax_cols(x), oracle.amax_tensor(x)
+    assert (ra == ta).all() and (ca == ta).all()
+    for bound in BOUNDS:
+        r_line = oracle.quantize_rowwise(x, oracle.MODE_LINE, ra, bound)
+        r_tens = oracle.quantize_rowwise(x, oracle.MODE_TENSOR, [ta], bound)
+        c_line = oracle.quantize_colwise(x, oracle.MODE_LINE, ca, bound)
+        c_tens = oracle.quantize_colwise(x, oracle.MODE_TENSOR, [ta], bound)
+        for a, b in zip(r_line + c_line, r_tens + c_tens):
+            assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------- power-of-two row scaling
+@pytest.mark.parametrize("k", [-13, -1, 1, 7, 20])
+def test_power_of_two_row_scaling(k):
+    x = torch.randn(24, 80, generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).float().numpy()
+    y = x.copy()
+    y[5] *= np.float32(2.0 ** k)
+    for bound in BOUNDS:
+        ra_x, ra_y = oracle.amax_rows(x), oracle.amax_rows(y)
+        assert ra_y[5] == ra_x[5] * np.float32(2.0 ** k)
+        qx, sx = oracle.quantize_rowwise(x, oracle.MODE_LINE, ra_x, bound)
+        qy, sy = oracle.quantize_rowwise(y, oracle.MODE_LINE, ra_y, bound)
+        assert np.array_equal(qx, qy) and np.array_equal(sx, sy)
+        dx = oracle.dequantize(qx, sx, 24, 80, oracle.MODE_LINE, ra_x, bound)
+        dy = oracle.dequantize(qy, sy, 24, 80, oracle.MODE_LINE, ra_y, bound)
+        assert np.array_equal(dy[5], dx[5] * np.float32(2.0 ** k))
+        other = np.arange(24) != 5
+        assert np.array_equal(dy[other], dx[other])
+
+
+# ------------------------------------------------------------------ zero lines
+def test_all_zero_row_and_column():
+    x = _random_matrix(40, 64, seed=4)
+    x[9, :] = 0.0
+    x[:, 17] = 0.0
+    ra, ca = oracle.amax_rows(x), oracle.amax_cols(x)
+    assert ra[9] == 0 and ca[17] == 0
+    q, s = oracle.quantize_rowwise(x, oracle.MODE_LINE, ra, 448.0)
+    assert not q[9].any() and not s[9].any()
+    qc, sc = oracle.quantize_colwise(x, oracle.MODE_LINE, ca, 448.0)
+    assert not qc[17].any() and not sc[17].any()
+    y = oracle.dequantize(q, s, 40, 64, oracle.MODE_LINE, ra, 448.0)
+    assert not y[9].view(np.uint32).any()
+
+
+# ---------------------------------------------- the block holding the line amax
+@pytest.mark.parametrize("bound,byte", [(448.0, 0x7E), (256.0, 0x78)])
+def test_amax_block_scale_is_the_bound(bound, byte):
+    """s32 of the block holding a = max|x| is RN(RN(a/6) * RN(6*bound/a)),
+    within a few ulps of bound, so its E4M3 byte encodes the bound itself and
+    the element equal to a gets the top code (6) and dequantizes to a within
+    a few ulps."""
+    x = _random_matrix(50, 96, seed=5)
+    ra = oracle.amax_rows(x)
+    q, s = oracle.quantize_rowwise(x, oracle.MODE_LINE, ra, bound)
+    codes = _unpack_codes(q, 96)
+    y = oracle.dequantize(q, s, 50, 96, oracle.MODE_LINE, ra, bound)
+    for i in range(50):
+        j = int(np.argmax(np.abs(x[i])))
+        assert s[i, j // 16] == byte
+        assert codes[i, j] & 7 == 7
+        ulp = np.spacing(np.float32(ra[i]))
+        assert abs(abs(y[i, j]) - ra[i]) <= 4 * ulp
+
+
+# ------------------------------------------------------------- error bound
+@pytest.mark.parametrize("name", ["tiny_rowscale", "outliers", "fp32_edge"])
+def test_dequantized_error_bound(name):
+    shape = {"tiny_rowscale": None, "outliers": (256, 512), "fp32_edge": (97, 160)}[name]
+    w = workloads.make(name, shape)
+    x = _f32(w.x)
+    M, K = x.shape
+    ra = oracle.amax_rows(x)
+    for bound in BOUNDS:
+        q, s = oracle.quantize_rowwise(x, oracle.MODE_LINE, ra, bound)
+        y = oracle.dequantize(q, s, M, K, oracle.MODE_LINE, ra, bound).astype(np.float64)
+        f_inv = np.float32(oracle.factor_inv(bound))
+        sq = np.array([oracle.e4m3_value(b) for b in range(256)], dtype=np.float32)[s]
+        d = ((sq * ra[:, None]).astype(np.float32) * f_inv).astype(np.float32)
+        d = np.repeat(d, 16, axis=1)[:, :K].astype(np.float64)
+        err = np.abs(x.astype(np.float64) - y)
+        # enc = min(RN(1/D), FLT_MAX) is clamped when D < 1/FLT_MAX (a line
+        # whose amax is itself subnormal): codes then undershoot x/D, and only
+        # |y| <= |x| + D with y of the sign of x (or zero) remains.
+        clamped = (d > 0) & (d < 2.0 ** -128)
+        assert (np.abs(y[clamped]) <= np.abs(x[clamped]) + d[clamped]).all()
+        assert (y[clamped] * x[clamped] >= 0).all()
+        loose = np.maximum(d, np.abs(x) - 6 * d) * (1 + 2.0 ** -18) + 2.0 ** -146
+        assert (err[~clamped] <= loose[~clamped]).all()
+        # normal E4M3 scale and normal D: the error is at most one decode step
+        normal = (np.repeat(s, 16, axis=1)[:, :K] >= 8) & (d >= np.finfo(np.float32).tiny)
+        assert (err[normal] <= d[normal] * (1 + 2.0 ** -18) + 2.0 ** -146).all()
+
+
+# ------------------------------------------------------------ exact round trip
+@pytest.mark.parametrize("k", [-30, 0, 25])
+def test_grid_values_round_trip_exactly(k):
+    """a = 6 * 2^k and bound 448 give S_enc = 448 * 2^-k, byte 0x7E, D = 2^k,
+    enc = 2^-k: values on the E2M1 grid times 2^k come back bit-exact."""
+    rng = np.random.default_rng(k + 100)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)
+    x = grid[rng.integers(0, 8, size=(8, 64))] * np.where(rng.random((8, 64)) < 0.5, -1, 1)
+    x[:, ::16] = 6.0
+    x = (x * np.float32(2.0 ** k)).astype(np.float32)
+    ra = oracle.amax_rows(x)
+    q, s = oracle.quantize_rowwise(x, oracle.MODE_LINE, ra, 448.0)
+    assert (s == 0x7E).all()
+    y = oracle.dequantize(q, s, 8, 64, oracle.MODE_LINE, ra, 448.0)
+    assert np.array_equal(y, x)
+
+
+# ------------------------------------------------- grouped tokens (MoE) invariants
+def test_group_expanded_quantize_equals_per_split():
+    """torchao grouped-GEMM PR description: the group amaxes expand to a
+    per-row amax vector so that one quantize call is bitwise identical to
+    quantizing each split separately; padded rows quantize to zero codes."""
+    w = workloads.moe_groups((700, 64), n_groups=5, align=32)
+    x = _f32(w.x)
+    M, K = x.shape
+    ge = w.group_end.numpy()
+    ra = oracle.amax_rows(x)
+    ex = oracle.group_amax_expand(ra, ge)
+    for bound in BOUNDS:
+        q, s = oracle.quantize_rowwise(x, oracle.MODE_LINE, ex, bound)
+        qc, sc = oracle.quantize_colwise(x, oracle.MODE_ROWGROUP, ex, bound)
+        start = 0
+        for g, end in enumerate(ge):
+            xs = x[start:end]
+            if end > start:
+                ta = oracle.amax_tensor(xs)
+                qs, ss = oracle.quantize_rowwise(xs, oracle.MODE_TENSOR, [ta], bound)
+                assert np.array_equal(q[start:end], qs) and np.array_equal(s[start:end], ss)
+                qcs, scs = oracle.quantize_colwise(xs, oracle.MODE_TENSOR, [ta], bound)
+                assert np.array_equal(qc[:, start // 2:end // 2], qcs)
+                assert np.array_equal(sc[:, start // 16:end // 16], scs)
+                real = start + int(w.group_rows[g])
+                assert not q[real:end].any() and not s[real:end].any()
+            start = end
+
+
+def test_ragged_padded_equals_aligned_construction():
+    """Zero-padding a ragged group to the alignment only appends zero rows:
+    the real rows' rowwise bytes equal those of the unpadded group."""
+    w = workloads.moe_groups((300, 48), n_groups=3, align=128)
+    x = _f32(w.x)
+    ge = w.group_end.numpy()
+    ex = oracle.group_amax_expand(oracle.amax_rows(x), ge)
+    q, s = oracle.quantize_rowwise(x, oracle.MODE_LINE, ex, 448.0)
+    start = 0
+    for g, end in enumerate(ge):
+        n = int(w.group_rows[g])
+        xs = x[start:start + n]
+        if n:
+            ta = oracle.amax_tensor(xs)
+            qs, ss = oracle.quantize_rowwise(xs, oracle.MODE_TENSOR, [ta], 448.0)
+            assert np.array_equal(q[start:start + n], qs) and np.array_equal(s[start:start + n], ss)
+        start = end
