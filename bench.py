@@ -1,0 +1,230 @@
+"""Throughput of row-scaled NVFP4 quantize-transpose on one MI355X.
+
+One step = the whole quantize path on one 8192 x 28672 BF16 matrix (the MLP
+activation / weight shape, N(0,1) times a per-row factor 10^U(-2,2)):
+  1. noop-aware zeroing of the amax vectors          (amax-init kernel)
+  2. fused per-row + per-column amax, one read of X   (fused amax kernel)
+  3. both NVFP4 copies (rowwise + transposed), one more read of X (cast kernel)
+The input is resident in HBM before timing starts. value = algorithmic bytes
+of the step (X read twice, amax vectors written and read once, all codes and
+scales written once) / step time, in GB/s.
+
+Also reported: per-kernel times, the cast kernel's fraction of the HBM
+roofline (8 TB/s), the dequantize kernel's bandwidth, a noop=1 check, and the
+CPU oracle timed on a bounded sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       python bench.py --copy-calibration   (plain torch copy, for counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+METRIC = "row-scaled NVFP4 quantize-transpose GB/s (in+out) and % of HBM peak, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cast_llm_mlp_traffic.json")
+
+
+def source_digest() -> str:
+    """Digest of the kernel sources: counter-derived traffic is only reported
+    for the kernel build it was measured on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "precision_quantization_row_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("cast_hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="rows of the workload the CPU oracle is timed on")
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+
+    n = 1 << 28  # 1 GiB of float32 read + 1 GiB written per copy
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the quantize path has no cross-GPU step in this build", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import precision_quantization_row_amd as p
+    from precision_quantization_row_amd import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    p.load_library()
+    w = workloads.make("llm_mlp")
+    M, K = w.shape
+    x = w.x.to(dev)
+    ra = torch.empty(M, dtype=torch.float32, device=dev)
+    ca = torch.empty(K, dtype=torch.float32, device=dev)
+    out = p.empty_outputs(M, K, dev)
+    bound = 448.0
+    assert p.nvfp4_amax_path(p.NVFP4_BF16, M, K, 1, 1, 0) == 1  # fused amax runs
+
+    def amax():
+        p.nvfp4_amax_rowcol(x, ra, ca)
+
+    def cast():
+        p.nvfp4_quantize_transpose(x, p.NVFP4_AMAX_LINE, ra, p.NVFP4_AMAX_LINE, ca, bound,
+                                   out["q_row"], out["s_row"], out["q_col"], out["s_col"])
+
+    for _ in range(args.warmup):
+        amax()
+        cast()
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K_steps):
+        ev[i][0].record()
+        amax()
+        ev[i][1].record()
+        cast()
+        ev[i][2].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    amax_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K_steps)]
+    cast_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K_steps)]
+    ms_per_step = total_ms / K_steps
+    step_bytes = workloads.algorithmic_bytes(M, K, 2)
+    cast_bytes = M * K * 2 + 4 * (M + K) + (M * ((K + 1) // 2) + M * ((K + 15) // 16)
+                                            + K * ((M + 1) // 2) + K * ((M + 15) // 16))
+    amax_bytes = M * K * 2 + 4 * (M + K)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    cast_avg = sum(cast_ms) / K_steps
+    cast_gbs = cast_bytes / (cast_avg * 1e-3) / 1e9
+    amax_avg = sum(amax_ms) / K_steps
+
+    # noop = 1: the amax state and the outputs survive a skipped call
+    noop = torch.ones(1, device=dev)
+    keep = (ra.clone(), ca.clone(), out["q_col"][:64].clone())
+    p.nvfp4_amax_rowcol(x, ra, ca, noop=noop)
+    p.nvfp4_quantize_transpose(x, 1, ra, 1, ca, bound, out["q_row"], out["s_row"],
+                               out["q_col"], out["s_col"], noop=noop)
+    torch.cuda.synchronize()
+    noop_ok = bool(torch.equal(keep[0], ra) and torch.equal(keep[1], ca)
+                   and torch.equal(keep[2], out["q_col"][:64]))
+
+    # dequantize the rowwise copy to BF16 (reported beside the step, not in it)
+    y = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        p.nvfp4_dequantize(out["q_row"], out["s_row"], M, K, 1, ra, bound, y)
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    nd = 10
+    d0.record()
+    for _ in range(nd):
+        p.nvfp4_dequantize(out["q_row"], out["s_row"], M, K, 1, ra, bound, y)
+    d1.record()
+    torch.cuda.synchronize()
+    dq_ms = d0.elapsed_time(d1) / nd
+    dq_bytes = M * ((K + 1) // 2) + M * ((K + 15) // 16) + 4 * M + M * K * 2
+    del y
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        rows = min(args.cpu_rows, M)
+        xs = w.x[:rows].float().numpy()
+        t0 = time.perf_counter()
+        ra_o, ca_o = oracle.amax_rows(xs), oracle.amax_cols(xs)
+        oracle.quantize_rowwise(xs, oracle.MODE_LINE, ra_o, bound)
+        oracle.quantize_colwise(xs, oracle.MODE_LINE, ca_o, bound)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(workloads.algorithmic_bytes(rows, K, 2) / dt / 1e9, 4),
+               "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": f"first {rows} rows x {K} columns of the same matrix as its own "
+                         f"{rows}x{K} input: amax rows+cols, both directions, "
+                         f"{dt:.2f} s wall"}
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llm_mlp: 8192x28672 BF16, N(0,1) x per-row 10^U(-2,2), "
+                               "row-scaled NVFP4 both directions, 1x16 blocks, bound 448",
+                   "M": M, "K": K, "input_dtype": "bf16", "step_bytes": step_bytes,
+                   "parallelism": "none (1 GPU)"},
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(cast_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(cast_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(), "kernel": "cast_kernel (quantize-transpose)",
+                     "bytes_per_launch": cast_bytes, "avg_us": round(cast_avg * 1e3, 2)},
+        "kernels_us": {"amax_init+fused_amax": round(amax_avg * 1e3, 2),
+                       "cast": round(cast_avg * 1e3, 2),
+                       "amax_GBs": round(amax_bytes / (amax_avg * 1e-3) / 1e9, 1)},
+        "dequant_rowwise_bf16": {"us": round(dq_ms * 1e3, 2),
+                                 "GBs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1)},
+        "noop_preserved": noop_ok,
+        "cpu_baseline": cpu,
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

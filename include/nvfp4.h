@@ -1,0 +1,151 @@
+/*
+ * nvfp4.h -- C ABI of libnvfp4.so: row-scaled NVFP4 quantize-transpose on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources: TransformerEngine PR "NVFP4: enable row-scaled
+ * transpose quantization for backward" -- summary and sequence diagram;
+ * TransformerEngine PR "row-scaled nvfp4 path: fuse row/col amax into a
+ * single TMA-tiled kernel" -- commit message, flowchart, host-wrapper review,
+ * description; torchao PR "Add NVFP4 four-over-six grouped GEMM for MoE
+ * training" -- description; torchao PR "Add backward overrides and 1x16
+ * weights to NVFP4 four-over-six" -- description):
+ *
+ *   X is an M x K row-major matrix (BF16 or FP32). A "line" is a row of X
+ *   (rowwise copy, length K) or a column of X (columnwise / transposed copy,
+ *   length M). Each line is cut into 1x16 blocks (the last one may be short).
+ *   a      = the line's second-level amax (per tensor, per line, or per group)
+ *   S_enc  = a == 0 ? 1 : min(RN(F / a), FLT_MAX),  F = RN(bound * 6)
+ *   bamax  = max |x| over the block
+ *   byte   = E4M3_RNE(min(RN(RN(bamax / 6) * S_enc), 448))   (stored scale)
+ *   D      = RN(RN(e4m3(byte) * a) * F_inv),       F_inv = RN(1 / F)
+ *   enc    = D == 0 ? 0 : min(RN(1 / D), FLT_MAX)
+ *   code   = E2M1_RNE_SATFINITE(RN(x * enc)), sign bit kept (so -0 -> 0x8)
+ *   dequantize: y = RN(e2m1(code) * D)   (BF16 output: RNE of the FP32 y)
+ * Every step is one IEEE binary32 operation rounded to nearest even, with
+ * subnormals kept. The decode D is the pages' (scale * amax) * factor_inv;
+ * the remaining op order, the zero-scale rule and the rounding rules are
+ * readings of pages that leave them open.
+ *
+ * Layouts (all packed, no pitch, no GEMM swizzle):
+ *   rowwise codes   q_row [M][ceil(K/2)]  element 2t in the low nibble
+ *   rowwise scales  s_row [M][ceil(K/16)] E4M3 bytes
+ *   colwise codes   q_col [K][ceil(M/2)]  (the transpose: column j of X)
+ *   colwise scales  s_col [K][ceil(M/16)]
+ *   A missing last high nibble (odd line length) is written as 0.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device memory of the current HIP device, owned by the
+ *     caller. The library allocates nothing and keeps no device state, so
+ *     calls on different streams never share scratch.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls only enqueue
+ *     work; nothing synchronizes and the host never reads device data.
+ *   - `noop` is NULL or a device pointer to one float. If *noop == 1.0f when
+ *     the kernels run, the call has no observable effect on any buffer
+ *     (amax buffers included); any other value runs normally.
+ *   - Arguments are validated before anything is enqueued; a rejected call
+ *     returns NVFP4_ERR_ARG / NVFP4_ERR_UNSUPPORTED and changes nothing.
+ *     A failed launch returns NVFP4_ERR_HIP.
+ *   - Inputs must be finite; NaN / +-inf are outside the contract. The
+ *     second-level amax must stay below FLT_MAX / 448 so that scale * amax
+ *     is finite.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_ARG = -1,         /* bad pointer, size, enum or bound           */
+  NVFP4_ERR_UNSUPPORTED = -2, /* valid request this build cannot serve      */
+  NVFP4_ERR_HIP = -3          /* the HIP runtime reported a launch failure  */
+} nvfp4_status;
+
+typedef enum { NVFP4_BF16 = 0, NVFP4_FP32 = 1 } nvfp4_dtype;
+
+typedef enum {
+  NVFP4_AMAX_TENSOR = 0,  /* amax[0] for every line (per-tensor NVFP4)       */
+  NVFP4_AMAX_LINE = 1,    /* amax[line]: row-scaled ([M] rows / [K] columns) */
+  NVFP4_AMAX_ROWGROUP = 2 /* transposed copy of grouped tokens: block b of a
+                             column uses amax[16*b], an [M] per-row vector of
+                             group amaxes (groups must start on 16-row
+                             boundaries for this to equal per-group calls)   */
+} nvfp4_amax_mode;
+
+enum { NVFP4_FLAG_FORCE_TWO_KERNEL = 1u }; /* skip the fused amax kernel */
+
+/* Which amax kernels nvfp4_amax_rowcol runs for these arguments.
+ * Returns 1 for the fused row+column pass, 2 for the separate row / column
+ * kernels, 0 when neither vector is requested. Host-only; enqueues nothing.
+ * The fused pass runs only for BF16 input with M % 128 == 0, K % 128 == 0,
+ * both row and column vectors requested, the flag clear and the environment
+ * variable NVFP4_FUSED_AMAX not set to "0" (the gate and kill switch of the
+ * fused-amax PR description). Both paths give identical bits (exact max). */
+int nvfp4_amax_path(int in_dtype, int64_t M, int64_t K, int want_row, int want_col,
+                    unsigned flags);
+
+/* Per-row, per-column and/or per-tensor amax of X (the pre-pass of the
+ * two-pass design: fused-amax PR commit message and description; sequence
+ * diagram of the row-scaled backward PR).
+ *   x           [M][K] BF16 or FP32, 16-byte aligned for the vector paths
+ *   row_amax    [M] float or NULL:  row_amax[i] = max_j |x_ij|
+ *   col_amax    [K] float or NULL:  col_amax[j] = max_i |x_ij|
+ *   tensor_amax [1] float or NULL:  max over all of X
+ * At least one output must be non-NULL. Outputs are overwritten (a noop-aware
+ * kernel zeroes them on the device, then the reductions publish with atomic
+ * max), never accumulated across calls. M, K >= 1. */
+int nvfp4_amax_rowcol(const void* x, int in_dtype, int64_t M, int64_t K, float* row_amax,
+                      float* col_amax, float* tensor_amax, const float* noop, unsigned flags,
+                      void* stream);
+
+/* Group amax expansion for grouped (MoE) tokens (grouped-GEMM PR
+ * description: per-group global scales, the group amaxes expanded to a
+ * per-row amax vector). In place on row_amax [M]: group g holds rows
+ * [group_end[g-1], group_end[g]) with group_end[-1] = 0, and every row of a
+ * group receives the max of the group's entries. group_end is a device int64
+ * array [G], non-decreasing, last entry <= M; entries are clamped to [0, M]
+ * on the device, so a bad array cannot cause an out-of-bounds access. Rows
+ * past group_end[G-1] are left unchanged. G >= 1. */
+int nvfp4_group_amax_expand(float* row_amax, int64_t M, const int64_t* group_end, int64_t G,
+                            const float* noop, void* stream);
+
+/* Quantize X into the rowwise copy, the columnwise (transposed) copy, or
+ * both, in one pass over X (row-scaled backward PR summary: the columnwise
+ * output is emitted in the same kernel pass with its own per-column amax).
+ *   row_mode / row_amax: TENSOR ([1]) or LINE ([M]); used if q_row != NULL
+ *   col_mode / col_amax: TENSOR ([1]), LINE ([K]) or ROWGROUP ([M]); used if
+ *                        q_col != NULL
+ *   bound: the E4M3 scale bound, finite, 0 < bound <= 448 (448 and 256 are
+ *          the tested values: grouped-GEMM PR, "bound-aware")
+ *   q_row [M][ceil(K/2)] and s_row [M][ceil(K/16)] (both or neither)
+ *   q_col [K][ceil(M/2)] and s_col [K][ceil(M/16)] (both or neither)
+ * At least one copy must be requested. Every byte of the requested outputs
+ * is written (unless noop). */
+int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
+                             const float* row_amax, int col_mode, const float* col_amax,
+                             float bound, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                             uint8_t* s_col, const float* noop, void* stream);
+
+/* Dequantize one packed copy (backward-overrides PR description: the inverse
+ * (scale * amax) * factor_inv with a correctly rounded FP32 reciprocal,
+ * per-tensor and row-scaled, BF16 or FP32 output).
+ *   q [R][ceil(C/2)], sc [R][ceil(C/16)]: a rowwise copy (R = M, C = K) or a
+ *       columnwise copy (R = K, C = M)
+ *   amax_mode / amax: TENSOR ([1]), LINE ([R]) or ROWGROUP ([C])
+ *   y [R][C] of out_dtype (NVFP4_BF16 or NVFP4_FP32). */
+int nvfp4_dequantize(const uint8_t* q, const uint8_t* sc, int64_t R, int64_t C, int amax_mode,
+                     const float* amax, float bound, void* y, int out_dtype, const float* noop,
+                     void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* nvfp4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

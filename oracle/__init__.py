@@ -62,6 +62,7 @@ def _load():
         "orc_group_amax_expand": (None, [f32p, i64p, i64, f32p]),
         "orc_e2m1_encode_array": (None, [f32p, i64, u8p]),
         "orc_e4m3_encode_array": (None, [f32p, i64, u8p]),
+        "orc_max_threads": (c_int, []),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -80,6 +81,11 @@ def _f32(a) -> np.ndarray:
 
 def _p(a: np.ndarray, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's line loops use."""
+    return int(_load().orc_max_threads())
 
 
 # --------------------------------------------------------------------------- formats

@@ -325,3 +325,11 @@ void orc_e4m3_encode_array(const float *v, int64_t n, uint8_t *out) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(v[i]);
 }
+
+/* Threads the OpenMP loops above use (reported next to oracle timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int orc_max_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_max_threads(void) { return 1; }
+#endif

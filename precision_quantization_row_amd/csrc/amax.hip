@@ -1,0 +1,374 @@
+// amax.hip -- the amax pre-pass of row-scaled NVFP4 (gfx950).
+//
+// The two-pass design (TransformerEngine row-scaled backward PR, sequence
+// diagram: row amax [M] and column amax [K] are computed before the cast) and
+// its fused form (fused-amax PR commit message: one pass computes both
+// directions, so the column reduction never reads global memory
+// column-strided). amax is an exact max, so every kernel here produces the
+// same bits whatever the reduction order; the fused and the separate kernels
+// are interchangeable (fused-amax PR description).
+//
+// Publication: a magnitude's fp32 bit pattern orders like the magnitude, so
+// partial maxima are published with 32-bit unsigned atomic max onto buffers a
+// noop-aware kernel has zeroed on the device (never a host memset: the
+// fused-amax PR review found that clearing before a skipped call destroys the
+// preserved amax state).
+#include "nvfp4_device.h"
+#include "nvfp4_launch.h"
+
+#include <algorithm>
+
+namespace nvfp4 {
+
+__device__ __forceinline__ bool skip(const float* noop) { return noop != nullptr && *noop == 1.0f; }
+
+// ------------------------------------------------------------------ init
+__global__ void __launch_bounds__(256) amax_init_kernel(float* ra, int64_t M, float* ca, int64_t K,
+                                                        float* ta, const float* noop) {
+  if (skip(noop)) return;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (ra)
+    for (int64_t i = t0; i < M; i += stride) ra[i] = 0.0f;
+  if (ca)
+    for (int64_t i = t0; i < K; i += stride) ca[i] = 0.0f;
+  if (ta && t0 == 0) ta[0] = 0.0f;
+}
+
+// ------------------------------------------------------------- fused (BF16)
+// Workgroup = 4 waves; a wave's 16-lane DPP row g reads 16 x 16 B = 128
+// consecutive BF16 of one row per load, so every load instruction fetches 4
+// full 256-byte row segments. The tile is FUSED_TR rows x (128 * FUSED_NC)
+// columns; the 16 (wave, row-group) slots take rows slot, slot + 16, ...
+// Each lane keeps the running column max of its 8 * FUSED_NC columns in
+// registers as packed u16 magnitudes (v_pk_max_u16), so the column reduction
+// is a register reduction over rows -- no strided global read and no LDS
+// staging of the tile. Row maxima are reduced across the 16 lanes with DPP
+// and published per row; column maxima of the 16 slots meet once in LDS at the
+// end of the tile and are published per column.
+constexpr int FUSED_NC = 4;    // 128-column chunks per tile -> 512 columns
+constexpr int FUSED_TR = 256;  // rows per tile
+
+__global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __restrict__ x,
+                                                              int64_t M, int64_t K,
+                                                              float* __restrict__ ra,
+                                                              float* __restrict__ ca,
+                                                              const float* noop,
+                                                              int64_t tiles_c) {
+  if (skip(noop)) return;
+  __shared__ uint32_t colmax_s[16][FUSED_NC * 64 + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int q = lane & 15;           // lane within the DPP row
+  const int slot = (tid >> 6) * 4 + (lane >> 4);  // 0..15
+  const int64_t tile = blockIdx.x;
+  const int64_t r0 = (tile / tiles_c) * FUSED_TR;
+  const int64_t c0 = (tile % tiles_c) * (128 * FUSED_NC);
+
+  uint32_t cm[FUSED_NC][4];
+#pragma unroll
+  for (int j = 0; j < FUSED_NC; ++j)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) cm[j][d] = 0u;
+
+  bool colok[FUSED_NC];
+#pragma unroll
+  for (int j = 0; j < FUSED_NC; ++j) colok[j] = (c0 + 128 * j) < K;  // K % 128 == 0
+
+  const int64_t rend = min(r0 + (int64_t)FUSED_TR, M);
+#pragma unroll 2
+  for (int64_t r = r0 + slot; r < rend; r += 16) {
+    const uint4* rowp = reinterpret_cast<const uint4*>(x + r * K + c0) + q;
+    uint4 v[FUSED_NC];
+#pragma unroll
+    for (int j = 0; j < FUSED_NC; ++j)
+      v[j] = colok[j] ? rowp[16 * j] : make_uint4(0, 0, 0, 0);
+    uint32_t rm = 0u;
+#pragma unroll
+    for (int j = 0; j < FUSED_NC; ++j) {
+      const uint32_t a0 = v[j].x & kAbsBf16x2, a1 = v[j].y & kAbsBf16x2;
+      const uint32_t a2 = v[j].z & kAbsBf16x2, a3 = v[j].w & kAbsBf16x2;
+      cm[j][0] = pk_max_u16(cm[j][0], a0);
+      cm[j][1] = pk_max_u16(cm[j][1], a1);
+      cm[j][2] = pk_max_u16(cm[j][2], a2);
+      cm[j][3] = pk_max_u16(cm[j][3], a3);
+      rm = pk_max_u16(rm, pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3)));
+    }
+    uint32_t rbits = max(rm & 0xFFFFu, rm >> 16) << 16;
+    rbits = row16_max(rbits);
+    if (q == 0) atomicMax(reinterpret_cast<unsigned int*>(ra + r), rbits);
+  }
+
+  // column maxima: the 16 slots meet in LDS, one atomic per column per tile
+#pragma unroll
+  for (int j = 0; j < FUSED_NC; ++j)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) colmax_s[slot][j * 64 + q * 4 + d] = cm[j][d];
+  __syncthreads();
+  // 256 threads, FUSED_NC * 64 dwords = 2 * FUSED_NC * 64 columns
+  for (int e = tid; e < FUSED_NC * 64; e += 256) {
+    uint32_t m = 0u;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) m = pk_max_u16(m, colmax_s[s][e]);
+    const int j = e / 64, w = e % 64;
+    const int64_t col = c0 + 128 * j + 2 * w;  // w = q * 4 + d -> columns 8q + 2d, +1
+    if (col < K) {
+      atomicMax(reinterpret_cast<unsigned int*>(ca + col), (m & 0xFFFFu) << 16);
+      atomicMax(reinterpret_cast<unsigned int*>(ca + col + 1), m & 0xFFFF0000u);
+    }
+  }
+}
+
+// -------------------------------------------------------------- row amax
+// One wave per row (grid-stride over rows); lanes stride the row with 16-byte
+// vectors when every row starts 16-byte aligned, else with scalar loads. The
+// wave owns its row, so the result is stored directly.
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256) row_amax_kernel(const T* __restrict__ x, int64_t M,
+                                                       int64_t K, float* __restrict__ ra,
+                                                       const float* noop) {
+  if (skip(noop)) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  constexpr int V = 16 / sizeof(T);
+  for (int64_t r = wave; r < M; r += nwaves) {
+    const T* row = x + r * K;
+    uint32_t m = 0u;
+    if (VEC) {
+      const uint4* rv = reinterpret_cast<const uint4*>(row);
+      const int64_t nv = K / V;
+      for (int64_t i = lane; i < nv; i += 64) {
+        const uint4 v = rv[i];
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t t = pk_max_u16(pk_max_u16(v.x & kAbsBf16x2, v.y & kAbsBf16x2),
+                                        pk_max_u16(v.z & kAbsBf16x2, v.w & kAbsBf16x2));
+          m = max(m, max(t & 0xFFFFu, t >> 16) << 16);
+        } else {
+          m = max(m, max(max(v.x & kAbsF32, v.y & kAbsF32), max(v.z & kAbsF32, v.w & kAbsF32)));
+        }
+      }
+      for (int64_t i = nv * V + lane; i < K; i += 64) {  // K % V tail (never with VEC rows)
+        if constexpr (sizeof(T) == 2)
+          m = max(m, (uint32_t)(reinterpret_cast<const uint16_t*>(row)[i] & 0x7FFFu) << 16);
+        else
+          m = max(m, reinterpret_cast<const uint32_t*>(row)[i] & kAbsF32);
+      }
+    } else {
+      for (int64_t i = lane; i < K; i += 64) {
+        if constexpr (sizeof(T) == 2)
+          m = max(m, (uint32_t)(reinterpret_cast<const uint16_t*>(row)[i] & 0x7FFFu) << 16);
+        else
+          m = max(m, reinterpret_cast<const uint32_t*>(row)[i] & kAbsF32);
+      }
+    }
+    // wave max
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if (lane == 0) ra[r] = __uint_as_float(m);
+  }
+}
+
+// ----------------------------------------------------------- column amax
+// Workgroup = 4 waves over one strip of columns; lane l owns columns
+// c0 + V*l .. +V (16-byte vector when rows are 16-byte aligned) or column
+// c0 + l (scalar). Each wave walks a quarter of the workgroup's row segment,
+// reading whole row segments (coalesced), and keeps the column max in
+// registers; the 4 waves meet in LDS and publish one atomic max per column.
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256) col_amax_kernel(const T* __restrict__ x, int64_t M,
+                                                       int64_t K, float* __restrict__ ca,
+                                                       const float* noop, int64_t rows_per_wg) {
+  if (skip(noop)) return;
+  constexpr int V = VEC ? (16 / sizeof(T)) : 1;
+  __shared__ uint32_t part[4][64 * V];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * 64 * V;
+  const int64_t rs = (int64_t)blockIdx.y * rows_per_wg;
+  const int64_t re = min(rs + rows_per_wg, M);
+  uint32_t m[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) m[k] = 0u;
+  const int64_t c = c0 + (int64_t)lane * V;
+  if (c < K) {
+    for (int64_t r = rs + w; r < re; r += 4) {
+      const T* p = x + r * K + c;
+      if constexpr (VEC) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            m[2 * d] = max(m[2 * d], (dw[d] & 0x7FFFu) << 16);
+            m[2 * d + 1] = max(m[2 * d + 1], dw[d] & 0x7FFF0000u);
+          }
+        } else {
+#pragma unroll
+          for (int d = 0; d < 4; ++d) m[d] = max(m[d], dw[d] & kAbsF32);
+        }
+      } else {
+        if constexpr (sizeof(T) == 2)
+          m[0] = max(m[0], (uint32_t)(*reinterpret_cast<const uint16_t*>(p) & 0x7FFFu) << 16);
+        else
+          m[0] = max(m[0], *reinterpret_cast<const uint32_t*>(p) & kAbsF32);
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < V; ++k) part[w][lane * V + k] = m[k];
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * V; e += 256) {
+    const uint32_t v = max(max(part[0][e], part[1][e]), max(part[2][e], part[3][e]));
+    const int64_t col = c0 + e;
+    if (col < K) atomicMax(reinterpret_cast<unsigned int*>(ca + col), v);
+  }
+}
+
+// ------------------------------------------------------------ tensor amax
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256) tensor_amax_kernel(const T* __restrict__ x, int64_t n,
+                                                          float* __restrict__ ta,
+                                                          const float* noop) {
+  if (skip(noop)) return;
+  __shared__ uint32_t red[4];
+  constexpr int V = 16 / sizeof(T);
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t m = 0u;
+  int64_t done = 0;
+  if (VEC) {
+    const uint4* xv = reinterpret_cast<const uint4*>(x);
+    const int64_t nv = n / V;
+    for (int64_t i = t0; i < nv; i += stride) {
+      const uint4 v = xv[i];
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t t = pk_max_u16(pk_max_u16(v.x & kAbsBf16x2, v.y & kAbsBf16x2),
+                                      pk_max_u16(v.z & kAbsBf16x2, v.w & kAbsBf16x2));
+        m = max(m, max(t & 0xFFFFu, t >> 16) << 16);
+      } else {
+        m = max(m, max(max(v.x & kAbsF32, v.y & kAbsF32), max(v.z & kAbsF32, v.w & kAbsF32)));
+      }
+    }
+    done = nv * V;
+  }
+  for (int64_t i = done + t0; i < n; i += stride) {
+    if constexpr (sizeof(T) == 2)
+      m = max(m, (uint32_t)(reinterpret_cast<const uint16_t*>(x)[i] & 0x7FFFu) << 16);
+    else
+      m = max(m, reinterpret_cast<const uint32_t*>(x)[i] & kAbsF32);
+  }
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t v = max(max(red[0], red[1]), max(red[2], red[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(ta), v);
+  }
+}
+
+// ----------------------------------------------------- group expansion
+// One workgroup per group: max over the group's rows, then every row of the
+// group receives it. Groups are disjoint, so the in-place update is safe.
+__global__ void __launch_bounds__(256) group_expand_kernel(float* __restrict__ ra, int64_t M,
+                                                           const int64_t* __restrict__ group_end,
+                                                           const float* noop) {
+  if (skip(noop)) return;
+  __shared__ uint32_t red[4];
+  const int64_t g = blockIdx.x;
+  int64_t s = g == 0 ? 0 : group_end[g - 1];
+  int64_t e = group_end[g];
+  s = min(max(s, (int64_t)0), M);
+  e = min(max(e, (int64_t)0), M);
+  uint32_t m = 0u;
+  for (int64_t i = s + threadIdx.x; i < e; i += 256) m = max(m, __float_as_uint(ra[i]) & kAbsF32);
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float v = __uint_as_float(max(max(red[0], red[1]), max(red[2], red[3])));
+  for (int64_t i = s + threadIdx.x; i < e; i += 256) ra[i] = v;
+}
+
+// ================================================================ launchers
+
+int launch_amax_init(float* ra, int64_t M, float* ca, int64_t K, float* ta, const float* noop,
+                     hipStream_t s) {
+  const int64_t n = max(ra ? M : 0, ca ? K : 0);
+  const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 1024));
+  hipLaunchKernelGGL(amax_init_kernel, dim3(blocks), dim3(256), 0, s, ra, M, ca, K, ta, noop);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_fused_amax_bf16(const void* x, int64_t M, int64_t K, float* ra, float* ca,
+                           const float* noop, hipStream_t s) {
+  const int64_t tiles_c = (K + 128 * FUSED_NC - 1) / (128 * FUSED_NC);
+  const int64_t tiles_r = (M + FUSED_TR - 1) / FUSED_TR;
+  hipLaunchKernelGGL(fused_amax_bf16_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), M, K, ra, ca, noop, tiles_c);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+template <typename T>
+static int launch_row_col_t(const void* xv, int64_t M, int64_t K, float* ra, float* ca,
+                            const float* noop, hipStream_t s) {
+  const T* x = static_cast<const T*>(xv);
+  constexpr int V = 16 / sizeof(T);
+  const bool vec = ((K % V) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  if (ra) {
+    const int64_t blocks = std::min<int64_t>((M + 3) / 4, (int64_t)num_cus() * 16);
+    if (vec)
+      hipLaunchKernelGGL((row_amax_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, s, x, M, K, ra, noop);
+    else
+      hipLaunchKernelGGL((row_amax_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, s, x, M, K, ra, noop);
+    if (hipGetLastError() != hipSuccess) return -3;
+  }
+  if (ca) {
+    const int64_t cols_per_wg = vec ? 64 * V : 64;
+    const int64_t strips = (K + cols_per_wg - 1) / cols_per_wg;
+    // enough row segments for ~8 workgroups per CU, at least 64 rows each
+    int64_t segs = std::max<int64_t>(1, ((int64_t)num_cus() * 8 + strips - 1) / strips);
+    segs = std::min<int64_t>(segs, std::max<int64_t>(1, (M + 63) / 64));
+    segs = std::min<int64_t>(segs, 65535);
+    const int64_t rows_per_wg = (M + segs - 1) / segs;
+    segs = (M + rows_per_wg - 1) / rows_per_wg;
+    dim3 grid((unsigned)strips, (unsigned)segs);
+    if (vec)
+      hipLaunchKernelGGL((col_amax_kernel<T, true>), grid, dim3(256), 0, s, x, M, K, ca, noop, rows_per_wg);
+    else
+      hipLaunchKernelGGL((col_amax_kernel<T, false>), grid, dim3(256), 0, s, x, M, K, ca, noop, rows_per_wg);
+    if (hipGetLastError() != hipSuccess) return -3;
+  }
+  return 0;
+}
+
+int launch_row_col_amax(const void* x, int in_dtype, int64_t M, int64_t K, float* ra, float* ca,
+                        const float* noop, hipStream_t s) {
+  return in_dtype == 0 ? launch_row_col_t<uint16_t>(x, M, K, ra, ca, noop, s)
+                       : launch_row_col_t<float>(x, M, K, ra, ca, noop, s);
+}
+
+template <typename T>
+static int launch_tensor_t(const void* xv, int64_t n, float* ta, const float* noop, hipStream_t s) {
+  const T* x = static_cast<const T*>(xv);
+  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  constexpr int V = 16 / sizeof(T);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n / V + 255) / 256, (int64_t)num_cus() * 8));
+  if (vec)
+    hipLaunchKernelGGL((tensor_amax_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, s, x, n, ta, noop);
+  else
+    hipLaunchKernelGGL((tensor_amax_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, s, x, n, ta, noop);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_tensor_amax(const void* x, int in_dtype, int64_t n, float* ta, const float* noop,
+                       hipStream_t s) {
+  return in_dtype == 0 ? launch_tensor_t<uint16_t>(x, n, ta, noop, s)
+                       : launch_tensor_t<float>(x, n, ta, noop, s);
+}
+
+int launch_group_expand(float* ra, int64_t M, const int64_t* group_end, int64_t G,
+                        const float* noop, hipStream_t s) {
+  hipLaunchKernelGGL(group_expand_kernel, dim3((unsigned)G), dim3(256), 0, s, ra, M, group_end, noop);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // namespace nvfp4

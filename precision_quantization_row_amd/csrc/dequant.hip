@@ -1,0 +1,114 @@
+// dequant.hip -- NVFP4 dequantize (gfx950).
+//
+// The inverse of one packed copy (torchao backward-overrides PR description:
+// the decode follows TransformerEngine's dequantize kernel, (scale * amax) *
+// factor_inv with a correctly rounded FP32 reciprocal, per-tensor and
+// row-scaled, BF16 or FP32 output):
+//   D   = RN(RN(e4m3(byte) * a) * F_inv)
+//   y_k = RN(e2m1(code_k) * D), BF16 output = RNE(y_k)
+// One thread per 1x16 block: 8 code bytes and 1 scale byte in, 16 values out.
+// Consecutive threads take consecutive blocks of a line, so the code loads
+// (8 B per lane) and the stores (32 B BF16 / 64 B FP32 per lane) are
+// contiguous across the wave.
+#include "nvfp4_device.h"
+#include "nvfp4_launch.h"
+
+#include <algorithm>
+
+namespace nvfp4 {
+
+// E4M3 byte -> float, exact. Low 7 bits: exponent field e, mantissa m;
+// e == 0: m * 2^-9, else (1 + m/8) * 2^(e-7) = fp32 pattern (byte + (120<<3)) << 20.
+__device__ __forceinline__ float e4m3_value(uint32_t byte) {
+  const uint32_t mag = byte & 0x7Fu;
+  const float v = mag < 8u ? (float)mag * 0x1p-9f : __uint_as_float((mag + (120u << 3)) << 20);
+  return (byte & 0x80u) ? -v : v;
+}
+
+// E2M1 code -> float, exact: magnitude field e = (c >> 1) & 3, mantissa m = c & 1;
+// e == 0: 0.5 m; else fp32 pattern ((e + 126) << 23) | (m << 22). Bit 3 = sign.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const uint32_t mag = e == 0u ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
+  return __uint_as_float(mag | ((c & 8u) << 28));
+}
+
+__device__ __forceinline__ uint32_t bf16_rne(float y) {
+  const uint32_t b = __float_as_uint(y);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256) dequant_kernel(const DequantArgs p, int64_t nb, int vec) {
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+  const int64_t R = p.R, C = p.C;
+  const int64_t qrs = (C + 1) / 2;
+  const int64_t total = R * nb;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t r = t / nb, b = t - (t / nb) * nb;
+    const float a = p.amax_mode == 0 ? p.amax[0] : (p.amax_mode == 1 ? p.amax[r] : p.amax[16 * b]);
+    const float d = (e4m3_value(p.sc[r * nb + b]) * a) * p.F_inv;
+    const int64_t c0 = 16 * b;
+    const bool full = vec && (c0 + 16 <= C);
+    uint32_t w0 = 0u, w1 = 0u;
+    const uint8_t* qp = p.q + r * qrs + c0 / 2;
+    if (full) {
+      const uint2 v = *reinterpret_cast<const uint2*>(qp);
+      w0 = v.x;
+      w1 = v.y;
+    } else {
+      for (int k = 0; k < 8; ++k)
+        if (c0 + 2 * k < C) {
+          const uint32_t byte = qp[k];
+          if (k < 4) w0 |= byte << (8 * k);
+          else w1 |= byte << (8 * (k - 4));
+        }
+    }
+    float y[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t code = ((k < 8 ? w0 : w1) >> (4 * (k & 7))) & 0xFu;
+      y[k] = e2m1_value(code) * d;
+    }
+    if constexpr (OUT_BF16) {
+      uint16_t* out = static_cast<uint16_t*>(p.y) + r * C + c0;
+      if (full) {
+        uint32_t o[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = bf16_rne(y[2 * k]) | (bf16_rne(y[2 * k + 1]) << 16);
+        reinterpret_cast<uint4*>(out)[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        reinterpret_cast<uint4*>(out)[1] = make_uint4(o[4], o[5], o[6], o[7]);
+      } else {
+        for (int k = 0; k < 16; ++k)
+          if (c0 + k < C) out[k] = (uint16_t)bf16_rne(y[k]);
+      }
+    } else {
+      float* out = static_cast<float*>(p.y) + r * C + c0;
+      if (full) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          reinterpret_cast<float4*>(out)[k] = make_float4(y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]);
+      } else {
+        for (int k = 0; k < 16; ++k)
+          if (c0 + k < C) out[k] = y[k];
+      }
+    }
+  }
+}
+
+int launch_dequant(const DequantArgs& a, hipStream_t s) {
+  const int64_t nb = (a.C + 15) / 16;
+  const int64_t total = a.R * nb;
+  // vector path: every line starts 8-byte aligned in q and 16-byte aligned in y
+  const int vec = (a.C % 16 == 0) && ((reinterpret_cast<uintptr_t>(a.q) & 7) == 0) &&
+                  ((reinterpret_cast<uintptr_t>(a.y) & 15) == 0);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, (int64_t)num_cus() * 16));
+  if (a.out_dtype == 0)
+    hipLaunchKernelGGL((dequant_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, a, nb, vec);
+  else
+    hipLaunchKernelGGL((dequant_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, a, nb, vec);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,52 @@
+// nvfp4_launch.h -- host-side launchers shared by the C ABI (nvfp4_api.hip).
+// Each returns 0 on success or -3 (NVFP4_ERR_HIP) when the launch failed.
+// Arguments are validated by the caller before any of these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Compute units of the current device (cached per device).
+int num_cus();
+
+int launch_amax_init(float* ra, int64_t M, float* ca, int64_t K, float* ta, const float* noop,
+                     hipStream_t s);
+int launch_fused_amax_bf16(const void* x, int64_t M, int64_t K, float* ra, float* ca,
+                           const float* noop, hipStream_t s);
+int launch_row_col_amax(const void* x, int in_dtype, int64_t M, int64_t K, float* ra, float* ca,
+                        const float* noop, hipStream_t s);
+int launch_tensor_amax(const void* x, int in_dtype, int64_t n, float* ta, const float* noop,
+                       hipStream_t s);
+int launch_group_expand(float* ra, int64_t M, const int64_t* group_end, int64_t G,
+                        const float* noop, hipStream_t s);
+
+struct CastArgs {
+  const void* x;
+  int in_dtype;  // 0 BF16, 1 FP32
+  int64_t M, K;
+  int row_mode;
+  const float* row_amax;
+  int col_mode;
+  const float* col_amax;
+  float F, F_inv;
+  uint8_t *q_row, *s_row, *q_col, *s_col;
+  const float* noop;
+};
+int launch_cast(const CastArgs& a, hipStream_t s);
+
+struct DequantArgs {
+  const uint8_t* q;
+  const uint8_t* sc;
+  int64_t R, C;
+  int amax_mode;
+  const float* amax;
+  float F_inv;
+  void* y;
+  int out_dtype;  // 0 BF16, 1 FP32
+  const float* noop;
+};
+int launch_dequant(const DequantArgs& a, hipStream_t s);
+
+}  // namespace nvfp4

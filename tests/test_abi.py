@@ -1,0 +1,104 @@
+"""The C ABI library loads on the host and exports every entry point that
+include/nvfp4.h declares; host-side validation and the fused-amax gate work
+without a GPU (no call here enqueues device work: each is rejected before any
+HIP call, or is the host-only gate query)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_quantization_row_amd as p
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(p.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = p.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert hasattr(p, name), name  # the binding has the same names
+
+
+def test_status_strings():
+    assert p.status_string(p.NVFP4_OK) == "ok"
+    assert p.status_string(p.NVFP4_ERR_ARG) == "invalid argument"
+    assert p.status_string(p.NVFP4_ERR_HIP) == "HIP launch failure"
+
+
+@pytest.mark.parametrize("dtype,M,K,row,col,flags,want", [
+    (p.NVFP4_BF16, 256, 512, 1, 1, 0, 1),
+    (p.NVFP4_BF16, 8192, 28672, 1, 1, 0, 1),
+    (p.NVFP4_FP32, 256, 512, 1, 1, 0, 2),      # FP32 -> two kernels
+    (p.NVFP4_BF16, 257, 512, 1, 1, 0, 2),      # unaligned M
+    (p.NVFP4_BF16, 256, 520, 1, 1, 0, 2),      # unaligned K
+    (p.NVFP4_BF16, 256, 512, 1, 0, 0, 2),      # one direction only
+    (p.NVFP4_BF16, 256, 512, 0, 1, 0, 2),
+    (p.NVFP4_BF16, 256, 512, 1, 1, p.NVFP4_FLAG_FORCE_TWO_KERNEL, 2),
+    (p.NVFP4_BF16, 256, 512, 0, 0, 0, 0),
+])
+def test_fused_amax_gate(dtype, M, K, row, col, flags, want):
+    assert p.nvfp4_amax_path(dtype, M, K, row, col, flags) == want
+
+
+def test_fused_amax_kill_switch(monkeypatch):
+    monkeypatch.setenv("NVFP4_FUSED_AMAX", "0")
+    assert p.nvfp4_amax_path(p.NVFP4_BF16, 256, 512, 1, 1, 0) == 2
+    monkeypatch.setenv("NVFP4_FUSED_AMAX", "1")
+    assert p.nvfp4_amax_path(p.NVFP4_BF16, 256, 512, 1, 1, 0) == 1
+
+
+def _fake(addr=0x1000):
+    return ctypes.c_void_p(addr)  # never dereferenced: every call below is rejected first
+
+
+def test_validation_rejects_before_launch():
+    lib = p.load_library()
+    f = ctypes.c_float
+    E = p.NVFP4_ERR_ARG
+    # amax: null input, bad sizes, bad dtype, no output, unknown flag
+    assert lib.nvfp4_amax_rowcol(None, 0, 4, 4, _fake(), None, None, None, 0, None) == E
+    assert lib.nvfp4_amax_rowcol(_fake(), 0, 0, 4, _fake(), None, None, None, 0, None) == E
+    assert lib.nvfp4_amax_rowcol(_fake(), 0, 4, -1, _fake(), None, None, None, 0, None) == E
+    assert lib.nvfp4_amax_rowcol(_fake(), 7, 4, 4, _fake(), None, None, None, 0, None) == E
+    assert lib.nvfp4_amax_rowcol(_fake(), 0, 4, 4, None, None, None, None, 0, None) == E
+    assert lib.nvfp4_amax_rowcol(_fake(), 0, 4, 4, _fake(), None, None, None, 8, None) == E
+    # quantize: bounds outside (0, 448], NaN, missing buffers, bad modes
+    q = lambda bound, rm=1, cm=1, qr=_fake(), sr=_fake(), qc=_fake(), sc=_fake(), ra=_fake(), ca=_fake(): \
+        lib.nvfp4_quantize_transpose(_fake(), 0, 32, 32, rm, ra, cm, ca, f(bound), qr, sr, qc, sc, None, None)
+    for bad in (0.0, -1.0, 449.0, float("nan"), float("inf")):
+        assert q(bad) == E
+    assert q(448.0, qr=None, sr=None, qc=None, sc=None) == E
+    assert q(448.0, sr=None) == E
+    assert q(448.0, sc=None) == E
+    assert q(448.0, ra=None) == E
+    assert q(448.0, rm=2) == E      # ROWGROUP is for the transposed copy only
+    assert q(448.0, cm=3) == E
+    # dequantize
+    d = lambda mode=1, out=0, bound=448.0, R=4, C=16: lib.nvfp4_dequantize(
+        _fake(), _fake(), R, C, mode, _fake(), f(bound), _fake(), out, None, None)
+    assert d(mode=5) == E
+    assert d(out=2) == E
+    assert d(bound=500.0) == E
+    assert d(R=0) == E
+    # group expansion
+    assert lib.nvfp4_group_amax_expand(_fake(), 16, _fake(), 0, None, None) == E
+    assert lib.nvfp4_group_amax_expand(None, 16, _fake(), 2, None, None) == E
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(16, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        p.nvfp4_amax_rowcol(x, torch.zeros(16))

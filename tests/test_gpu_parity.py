@@ -1,0 +1,201 @@
+"""GPU parity: every output of the HIP path, called through the C ABI, is
+compared element by element with the CPU oracle on the same seeded input.
+The bar is bit-exact for amax floats, E4M3 scale bytes, packed E2M1 code
+bytes (padding nibbles included) and dequantized FP32 / BF16 bits."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_quantization_row_amd as p
+from precision_quantization_row_amd import workloads
+
+from parity_utils import (assert_same, check_row_scaled, dequant_bits, f32_bits, gpu_amax,
+                          gpu_dequant, gpu_quantize, oracle_dequant_bits, say, to_np)
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    p.load_library()
+
+
+# ------------------------------------------------------- small shapes, full
+SMALL = [
+    ("tiny_rowscale", None),          # 256 x 256 BF16, fused amax
+    ("outliers", (384, 640)),         # BF16, fused amax, several tiles
+    ("llm_mlp", (512, 1152)),         # BF16, fused, partial 512-column strip
+    ("llm_mlp", (200, 520)),          # BF16 unaligned: two-kernel amax, ragged tiles
+    ("llm_mlp", (129, 1000)),         # BF16, M % 16 != 0, K % 16 != 0
+    ("fp32_edge", (97, 160)),         # FP32 ragged rows
+    ("fp32_edge", (33, 47)),          # FP32 odd sizes, odd line lengths
+    ("tiny_rowscale", (1, 1)),
+    ("tiny_rowscale", (1, 17)),
+    ("tiny_rowscale", (17, 1)),
+    ("tiny_rowscale", (2, 33)),
+]
+
+
+@pytest.mark.parametrize("name,shape", SMALL, ids=[f"{n}-{s}" for n, s in SMALL])
+def test_small_row_scaled(name, shape):
+    w = workloads.make(name, shape)
+    check_row_scaled(w.x, bounds=(448.0, 256.0), label=name)
+
+
+@pytest.mark.parametrize("shape", [(256, 256), (384, 640)])
+def test_small_forced_two_kernel(shape):
+    w = workloads.make("outliers", shape)
+    check_row_scaled(w.x, flags=p.NVFP4_FLAG_FORCE_TWO_KERNEL, dequant=False, label="two-kernel")
+
+
+def test_fused_equals_two_kernel_bytes():
+    """Fused-amax PR description: the fused pass is an exact max, so its
+    results are byte-identical to the two-kernel path."""
+    w = workloads.make("llm_mlp", (1024, 2048))
+    x = w.x.to(DEV)
+    assert p.nvfp4_amax_path(p.NVFP4_BF16, 1024, 2048, 1, 1, 0) == 1
+    ra1, ca1, _ = gpu_amax(x)
+    ra2, ca2, _ = gpu_amax(x, flags=p.NVFP4_FLAG_FORCE_TWO_KERNEL)
+    assert_same("row", f32_bits(ra1), f32_bits(ra2))
+    assert_same("col", f32_bits(ca1), f32_bits(ca2))
+
+
+def test_tensor_amax_and_per_tensor_quantize():
+    w = workloads.make("outliers", (300, 200))
+    x = w.x.to(DEV)
+    xf = w.x.float().numpy()
+    _, _, ta = gpu_amax(x, row=False, col=False, tensor=True)
+    ta_o = oracle.amax_tensor(xf)
+    assert f32_bits(ta)[0] == np.float32(ta_o).view(np.uint32)
+    for bound in (448.0, 256.0):
+        out = gpu_quantize(x, p.NVFP4_AMAX_TENSOR, ta, p.NVFP4_AMAX_TENSOR, ta, bound)
+        qr, sr = oracle.quantize_rowwise(xf, oracle.MODE_TENSOR, [ta_o], bound)
+        qc, sc = oracle.quantize_colwise(xf, oracle.MODE_TENSOR, [ta_o], bound)
+        assert_same("q_row", to_np(out["q_row"]), qr)
+        assert_same("s_row", to_np(out["s_row"]), sr)
+        assert_same("q_col", to_np(out["q_col"]), qc)
+        assert_same("s_col", to_np(out["s_col"]), sc)
+
+
+@pytest.mark.parametrize("rowwise,colwise", [(True, False), (False, True)])
+def test_single_direction(rowwise, colwise):
+    w = workloads.make("tiny_rowscale", (96, 80))
+    x = w.x.to(DEV)
+    xf = w.x.float().numpy()
+    ra, ca, _ = gpu_amax(x, row=rowwise, col=colwise)
+    out = gpu_quantize(x, 1, ra, 1, ca, 448.0, rowwise=rowwise, colwise=colwise)
+    if rowwise:
+        q, s = oracle.quantize_rowwise(xf, 1, oracle.amax_rows(xf), 448.0)
+        assert_same("q_row", to_np(out["q_row"]), q)
+        assert_same("s_row", to_np(out["s_row"]), s)
+    else:
+        q, s = oracle.quantize_colwise(xf, 1, oracle.amax_cols(xf), 448.0)
+        assert_same("q_col", to_np(out["q_col"]), q)
+        assert_same("s_col", to_np(out["s_col"]), s)
+
+
+# ------------------------------------------------------------ dequant matrix
+@pytest.mark.parametrize("bound", [448.0, 256.0])
+@pytest.mark.parametrize("mode", [p.NVFP4_AMAX_TENSOR, p.NVFP4_AMAX_LINE])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
+def test_dequant_matrix(bound, mode, out_dtype):
+    """Backward-overrides PR validation: 256/448 x per-tensor/row-scaled x
+    bf16/fp32 output."""
+    w = workloads.make("tiny_rowscale", (160, 272))
+    x = w.x.to(DEV)
+    xf = w.x.float().numpy()
+    M, K = xf.shape
+    if mode == p.NVFP4_AMAX_TENSOR:
+        _, _, a = gpu_amax(x, row=False, col=False, tensor=True)
+        a_o = np.array([oracle.amax_tensor(xf)], dtype=np.float32)
+    else:
+        a, _, _ = gpu_amax(x, col=False)
+        a_o = oracle.amax_rows(xf)
+    out = gpu_quantize(x, mode, a, mode, a, bound, colwise=False)
+    q, s = oracle.quantize_rowwise(xf, mode, a_o, bound)
+    assert_same("q_row", to_np(out["q_row"]), q)
+    y = gpu_dequant(out["q_row"], out["s_row"], M, K, mode, a, bound, out_dtype)
+    assert_same("dequant", dequant_bits(y), oracle_dequant_bits(q, s, M, K, mode, a_o, bound, out_dtype))
+
+
+def test_dequant_random_codes_all_bytes():
+    """Every code nibble and every finite non-negative scale byte."""
+    R, C = 127, 160
+    g = torch.Generator().manual_seed(9)
+    q = torch.randint(0, 256, (R, C // 2), generator=g, dtype=torch.uint8)
+    s = torch.randint(0, 127, (R, C // 16), generator=g, dtype=torch.uint8)
+    s.view(-1)[:127] = torch.arange(127, dtype=torch.uint8)
+    a = (torch.rand(R, generator=g) * 100).float()
+    for od in (torch.bfloat16, torch.float32):
+        y = gpu_dequant(q.to(DEV), s.to(DEV), R, C, p.NVFP4_AMAX_LINE, a.to(DEV), 448.0, od)
+        assert_same(f"dequant {od}", dequant_bits(y),
+                    oracle_dequant_bits(q.numpy(), s.numpy(), R, C, 1, a.numpy(), 448.0, od))
+
+
+# ---------------------------------------------------------------- noop
+def test_noop_leaves_every_buffer_untouched():
+    """Fused-amax PR review: a call skipped by noop must not erase the
+    preserved amax state -- nor any other output."""
+    w = workloads.make("outliers", (256, 512))
+    x = w.x.to(DEV)
+    noop = torch.ones(1, device=DEV)
+    for flags in (0, p.NVFP4_FLAG_FORCE_TWO_KERNEL):
+        ra, ca, ta = gpu_amax(x, tensor=True, flags=flags, noop=noop)
+        torch.cuda.synchronize()
+        assert (ra == -7.0).all() and (ca == -7.0).all() and (ta == -7.0).all()
+    ra, ca, _ = gpu_amax(x)
+    before = [t.clone() for t in (ra, ca)]
+    p.nvfp4_amax_rowcol(x, ra, ca, noop=noop)
+    assert all(torch.equal(a, b) for a, b in zip(before, (ra, ca)))
+    out = gpu_quantize(x, 1, ra, 1, ca, 448.0, noop=noop)
+    torch.cuda.synchronize()
+    for k, v in out.items():
+        assert (v == 0xA5).all(), k
+    y = torch.full((256, 512), 3.0, device=DEV)
+    q = torch.zeros(256, 256, dtype=torch.uint8, device=DEV)
+    s = torch.zeros(256, 32, dtype=torch.uint8, device=DEV)
+    p.nvfp4_dequantize(q, s, 256, 512, 1, ra, 448.0, y, noop=noop)
+    ge = torch.tensor([100, 256], dtype=torch.int64, device=DEV)
+    r2 = ra.clone()
+    p.nvfp4_group_amax_expand(r2, ge, noop=noop)
+    torch.cuda.synchronize()
+    assert (y == 3.0).all() and torch.equal(r2, ra)
+
+
+@pytest.mark.parametrize("val", [0.0, 2.0, -1.0])
+def test_noop_other_values_run(val):
+    w = workloads.make("tiny_rowscale", (64, 64))
+    x = w.x.to(DEV)
+    noop = torch.full((1,), val, device=DEV)
+    ra, ca, _ = gpu_amax(x, noop=noop)
+    xf = w.x.float().numpy()
+    assert_same("row", f32_bits(ra), oracle.amax_rows(xf).view(np.uint32))
+
+
+# --------------------------------------------------------- grouped tokens
+def test_group_expand_matches_oracle():
+    g = torch.Generator().manual_seed(3)
+    ra = torch.rand(1000, generator=g) * 10
+    ge = torch.tensor([0, 128, 128, 384, 1000], dtype=torch.int64)
+    r = ra.to(DEV)
+    p.nvfp4_group_amax_expand(r, ge.to(DEV))
+    want = oracle.group_amax_expand(ra.numpy(), ge.numpy())
+    assert_same("expanded", f32_bits(r), want.view(np.uint32))
+
+
+def test_other_stream():
+    w = workloads.make("llm_mlp", (256, 1024))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        x = w.x.to(DEV)
+        ra, ca, _ = gpu_amax(x)
+        out = gpu_quantize(x, 1, ra, 1, ca, 448.0)
+    s.synchronize()
+    xf = w.x.float().numpy()
+    q, sc = oracle.quantize_colwise(xf, 1, oracle.amax_cols(xf), 448.0)
+    assert_same("q_col", to_np(out["q_col"]), q)
