@@ -21,22 +21,19 @@ ROOT = os.path.dirname(HERE)
 
 
 def library_path() -> str:
-    return os.path.join(HERE, "libnvfp4.so")
+    """The in-tree libnvfp4.so (NVFP4_LIBRARY may name another build of it)."""
+    return os.environ.get("NVFP4_LIBRARY") or os.path.join(HERE, "libnvfp4.so")
 
 
-def sources() -> list:
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-
-
-def build_library(verbose: bool = False) -> str:
+def build_library(verbose: bool = False, out: str = None, csrc: str = CSRC) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    out = library_path()
+    out = out or os.path.join(HERE, "libnvfp4.so")
     tmp = out + ".tmp"
     cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-ffp-contract=off", "-Wall",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *sources(), "-o", tmp]
+           "-I", os.path.join(ROOT, "include"), "-I", csrc,
+           *sorted(glob.glob(os.path.join(csrc, "*.hip"))), "-o", tmp]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

@@ -7,7 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "../../include/nvfp4.h"
+#include "nvfp4.h"
 #include "nvfp4_launch.h"
 
 namespace nvfp4 {

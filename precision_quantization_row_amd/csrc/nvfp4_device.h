@@ -54,61 +54,69 @@ __device__ __forceinline__ float global_encode_scale(float a, float F) {
   return fminf(F / a, kFltMax);
 }
 
-// E4M3 (OCP E4M3FN) round-to-nearest-even of s in [0, 448]. Returns the byte
-// and its exact value in *decoded.
-//  s <  2^-6: the subnormal grid m * 2^-9, m = RNE(s * 2^9) in 0..8 (8 is the
-//             smallest normal, byte 0x08, so the carry is seamless)
-//  s >= 2^-6: keep 3 mantissa bits of the fp32 pattern with RNE; a carry into
-//             the exponent is the correct next binade; the exponent is rebiased
-//             from 127 to 7 by subtracting 120 << 3.
-__device__ __forceinline__ uint32_t e4m3_rne(float s, float* decoded) {
-  if (s < 0x1p-6f) {
-    const float m = rintf(s * 512.0f);
-    *decoded = m * 0x1p-9f;
-    return (uint32_t)m;
+// RN(x / 6) for x >= 0. For x >= 2^-125 the product with RN(1/6) is within
+// an ulp of x/6, its residual fma(-q, 6, x) is exact, and one correction step
+// gives the correctly rounded quotient (checked exhaustively on gfx950 against
+// the IEEE division for every finite x >= 2^-125); smaller x take the IEEE
+// division.
+__device__ __forceinline__ float div6_rn(float x) {
+  constexpr float kR6 = 0.16666667163372039794921875f;  // RN(1/6)
+  if (x >= 0x1p-125f) {
+    const float q = x * kR6;
+    return __builtin_fmaf(__builtin_fmaf(-q, kE2M1Max, x), kR6, q);
   }
-  const uint32_t b = __float_as_uint(s);
-  const uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
-  *decoded = __uint_as_float(r);
-  return (r >> 20) - (120u << 3);
+  return x / kE2M1Max;
+}
+
+// min(RN(1 / d), FLT_MAX) for d > 0. For d in [2^-126, 2^126) the hardware
+// reciprocal is within an ulp and one Newton step fma(fma(-d, r, 1), r, r)
+// lands on the correctly rounded value (checked exhaustively on gfx950 for
+// every d in that range); other d take the IEEE division.
+__device__ __forceinline__ float recip_rn(float d) {
+  if (d >= 0x1p-126f && d < 0x1p126f) {
+    const float r = __builtin_amdgcn_rcpf(d);
+    return __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+  }
+  return fminf(1.0f / d, kFltMax);
 }
 
 // One block: from its max magnitude, the line amax a, the line's S_enc and
-// F_inv, produce the stored E4M3 byte and the element encode factor.
+// F_inv, produce the stored E4M3 byte and the element encode factor:
+//   s32  = RN(RN(bamax / 6) * S_enc), clamped to 448 (also maps +inf to 448)
+//   byte = E4M3 round-to-nearest-even of s32 (v_cvt_pk_fp8_f32: OCP E4M3FN,
+//          equal to the RNE definition for every s32 in [0, 448], checked
+//          exhaustively on gfx950), sq = its exact value
+//   D    = RN(RN(sq * a) * F_inv)
+//   enc  = D == 0 ? 0 : min(RN(1 / D), FLT_MAX)
 __device__ __forceinline__ void block_scale(float bamax, float a, float s_enc, float f_inv,
                                             uint32_t* byte, float* enc) {
-  float s32 = (bamax / kE2M1Max) * s_enc;
-  s32 = fminf(s32, kE4M3Max);  // also maps +inf to 448
-  float sq;
-  *byte = e4m3_rne(s32, &sq);
+  const float s32 = fminf(div6_rn(bamax) * s_enc, kE4M3Max);
+  const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(s32, s32, 0, false);
+  *byte = (uint32_t)pk & 0xFFu;
+  const float sq = __builtin_amdgcn_cvt_f32_fp8(pk, 0);
   const float d = (sq * a) * f_inv;
-  *enc = (d == 0.0f) ? 0.0f : fminf(1.0f / d, kFltMax);
+  *enc = (d == 0.0f) ? 0.0f : recip_rn(d);
 }
 
 // --------------------------------------------------------------- E2M1 encode
-// Round-to-nearest-even onto {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at 6,
-// sign bit (bit 3) copied from v (so -0 and negatives rounding to 0 give 0x8).
-//  |v| < 1: code = RNE(2|v|) in 0..2 (0.25 -> 0, 0.75 -> 2: ties to even)
-//  |v| >= 1: keep 1 mantissa bit of the fp32 pattern with RNE; exponent
-//            rebias 127 -> 1 is a subtraction of 126 << 1; clamp to 7.
-__device__ __forceinline__ uint32_t e2m1_rne(float v) {
-  const uint32_t bits = __float_as_uint(v);
-  const uint32_t sign = (bits >> 28) & 8u;
-  const uint32_t mb = bits & kAbsF32;
-  const float m = __uint_as_float(mb);
-  uint32_t code;
-  if (m < 1.0f) {
-    code = (uint32_t)rintf(m * 2.0f);
-  } else {
-    const uint32_t t = (mb + 0x1FFFFFu + ((mb >> 22) & 1u)) >> 22;
-    code = min(t - 252u, 7u);
-  }
-  return sign | code;
-}
+// v_cvt_scalef32_pk_fp4_f32 with scale 1.0 converts two fp32 values to E2M1
+// with round-to-nearest-even, saturation at 6 and the sign bit kept (-0 and
+// negatives rounding to 0 give 0x8); this equals the definition for every
+// non-NaN fp32 input (checked exhaustively on gfx950). The first value lands
+// in the low nibble of byte SEL of the result, the second in the high nibble;
+// the other bytes of `old` pass through.
+#define NVFP4_CVT_FP4X2(old, v0, v1, SEL) \
+  __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (v0), (v1), 1.0f, (SEL))
 
-// Four elements -> four nibbles in the low 16 bits (element 0 lowest).
-__device__ __forceinline__ uint32_t e2m1_pack4(float v0, float v1, float v2, float v3) {
-  return e2m1_rne(v0) | (e2m1_rne(v1) << 4) | (e2m1_rne(v2) << 8) | (e2m1_rne(v3) << 12);
+// Eight elements -> one dword of eight nibbles (element k in nibble k).
+__device__ __forceinline__ uint32_t e2m1_pack8(float v0, float v1, float v2, float v3, float v4,
+                                               float v5, float v6, float v7) {
+  uint32_t w = 0u;
+  w = NVFP4_CVT_FP4X2(w, v0, v1, 0);
+  w = NVFP4_CVT_FP4X2(w, v2, v3, 1);
+  w = NVFP4_CVT_FP4X2(w, v4, v5, 2);
+  w = NVFP4_CVT_FP4X2(w, v6, v7, 3);
+  return w;
 }
 
 }  // namespace nvfp4
