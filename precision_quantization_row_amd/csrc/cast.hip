@@ -333,47 +333,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 // --------------------------------------------------------- interior kernel
-// Interior tiles: 128 rows x 512 columns, strip-major order, in runs walked
-// by persistent 8-wave workgroups (one per CU; runs adjacent in memory go to
-// workgroups on the same XCD, workgroup b running on XCD b % 8).
+// Interior tiles are 64 rows x 512 columns. A workgroup is 4 waves; wave w
+// holds rows r0 + 16w .. +16 of the tile and all 512 columns, lane l a 16 x 8
+// block at columns c0 + 8l, so every load instruction reads 1 KB of one row
+// and every rowwise-code store writes 256 contiguous bytes of one row.
 //
-// Wave w of a tile holds rows r0 + 16w .. +16 and all 512 columns: lane l a
-// 16 x 8 block at columns c0 + 8l. Every load instruction then reads 1 KB of
-// one row, and every rowwise-code store writes 256 contiguous bytes of one
-// row. The other outputs are transposed or small, and on this GPU a store's
-// write bandwidth depends on how long its contiguous runs are (a few bytes per
-// run give well under a quarter of what 128+ byte runs give), so they are
-// staged in LDS and leave as long runs written 16 or 8 bytes per lane:
-//   transposed codes  -- two tiles (256 rows): 128 B per column
-//   transposed scales -- eight tiles (1024 rows): 64 B per column
-//   rowwise scales    -- one tile: 32 B per row (the strip is 512 wide)
-// Partial chunks are flushed at the end of a run or of a strip. BF16 keeps
-// two register buffers: the next tile's rows are in flight while the current
-// tile is computed.
-constexpr int T5_WAVES = 8;
-constexpr int T5_ROWS = 16 * T5_WAVES;  // 128
-constexpr int T5_COLS = CAST_STRIP_COLS;  // 512
-constexpr int T5_QC_TILES = 2;          // transposed codes: 128 B per column
-constexpr int T5_SC_TILES = 8;          // transposed scales: 64 B per column
+// Schedule. On this GPU write bandwidth depends on how long the contiguous
+// runs that reach memory at about the same time are, far more than read
+// bandwidth does. The persistent workgroups therefore advance in lockstep
+// "super-steps": workgroup b runs on XCD x = b % 8 as its j = b / 8-th of
+// P = grid / 8 workgroups there, and in super-step u it takes strip
+// 8 * (u / nh) + x and tile row P * (u % nh) + j (nh = tile rows / P, rounded
+// up). At any moment the P (64 on MI355X) workgroups of an XCD cover P
+// consecutive tiles of one strip and the 8 XCDs cover 8 adjacent strips, so
+//   rowwise codes      -- one row gets 8 x 256 B = 2 KB in the same window
+//   transposed codes   -- one column gets 64 x 32 B = 2 KB, all from one XCD,
+//                         so its lines fill up in that XCD's L2
+//   scales             -- 256 B runs in both directions
+// Within a tile the transposed codes (32 B per column), transposed scales
+// (4 B per column) and rowwise scales (32 B per row) are gathered in LDS
+// (double buffered) and stored 16 bytes per lane where the run allows it.
+constexpr int T6_ROWS = 64;
+constexpr int T6_COLS = CAST_STRIP_COLS;  // 512
+constexpr int T6_XCDS = 8;
 
-struct T5Smem {
-  // transposed codes of up to 2 tiles: [tile][column][64 B = 8 waves x 8 B],
-  // the 8-byte slot of wave w stored at slot w ^ ((column >> 3) & 7)
-  uint8_t qc[T5_QC_TILES][T5_COLS][64];
-  // transposed scales of up to 8 tiles: [tile][column][8 B = 8 waves x 1 B]
-  uint8_t sc[T5_SC_TILES][T5_COLS][8];
-  // rowwise scales of one tile, double buffered: [buf][row][32 B]
-  uint8_t sr[2][T5_ROWS][32];
+struct T6Smem {
+  // transposed codes: [buf][column][4 waves x 8 B], wave w's slot at w ^ ((column >> 3) & 3)
+  uint8_t qc[2][T6_COLS][32];
+  // transposed scales: [buf][column][4 waves x 1 B]
+  uint8_t sc[2][T6_COLS][4];
+  // rowwise scales: [buf][row][32 B]
+  uint8_t sr[2][T6_ROWS][32];
   // per-wave row amax / S_enc of the wave's 16 rows
-  float ra[T5_WAVES][16], rs[T5_WAVES][16];
+  float ra[4][16], rs[4][16];
 };
 
-struct StoreT5 {
+struct StoreT6 {
   __amdgpu_buffer_rsrc_t qr;  // rowwise codes of this tile
   uint32_t vo_qr, qrs;
-  uint8_t* sr;  // this tile's rowwise-scale stage [128][32]
-  uint8_t* qc;  // this tile's transposed-code stage [512][64]
-  uint8_t* sc;  // this tile's transposed-scale stage [512][8]
+  uint8_t* sr;
+  uint8_t* qc;
+  uint8_t* sc;
   int wv, lane, par;
   __device__ __forceinline__ void row_codes(int i, uint32_t word) const {
     __builtin_amdgcn_raw_buffer_store_b32(word, qr, (int)vo_qr, (int)(i * qrs), 0);
@@ -383,17 +383,16 @@ struct StoreT5 {
   }
   __device__ __forceinline__ void col(int k, uint32_t w0, uint32_t w1, uint32_t byte) const {
     const int c = 8 * lane + k;
-    const int slot = wv ^ (lane & 7);
-    *reinterpret_cast<uint2*>(qc + c * 64 + slot * 8) = make_uint2(w0, w1);
-    sc[c * 8 + wv] = (uint8_t)byte;
+    *reinterpret_cast<uint2*>(qc + c * 32 + 8 * (wv ^ (lane & 3))) = make_uint2(w0, w1);
+    sc[c * 4 + wv] = (uint8_t)byte;
   }
 };
 
-template <typename T, bool ROWW, bool COLW, bool PREFETCH>
-__global__ void __launch_bounds__(512) cast_interior_kernel(const CastK p) {
+template <typename T, bool ROWW, bool COLW>
+__global__ void __launch_bounds__(256) cast_interior_kernel(const CastK p) {
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   constexpr int NW = Blk<T>::NW;
-  __shared__ __attribute__((aligned(16))) T5Smem sm;
+  __shared__ __attribute__((aligned(16))) T6Smem sm;
   const T* __restrict__ x = static_cast<const T*>(p.x);
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
@@ -401,160 +400,102 @@ __global__ void __launch_bounds__(512) cast_interior_kernel(const CastK p) {
   const int par = lane & 1;
   const int64_t K = p.K;
 
-  const int64_t ntiles = p.n_istrips * p.n_isteps;
-  const int64_t G = gridDim.x;  // a multiple of 8
-  const int64_t wg = blockIdx.x;
-  const int64_t run = (wg & 7) * (G >> 3) + (wg >> 3);
-  const int64_t t_begin = run * ntiles / G, t_end = (run + 1) * ntiles / G;
-  if (t_begin >= t_end) return;
+  const int64_t G = gridDim.x;  // T6_XCDS * per_xcd workgroups
+  const int64_t per_xcd = G / T6_XCDS;  // tiles of one strip an XCD covers per super-step
+  const int64_t xcd = blockIdx.x % T6_XCDS, jw = blockIdx.x / T6_XCDS;
+  const int64_t nstrips = p.n_istrips, ntrows = p.n_isteps;  // tile rows per strip
+  const int64_t nh = (ntrows + per_xcd - 1) / per_xcd;
+  const int64_t ng = (nstrips + T6_XCDS - 1) / T6_XCDS;
 
   const uint32_t rowbytes = (uint32_t)(K * (int64_t)sizeof(T));
   const int64_t qrs = (K + 1) / 2, srs = (K + 15) / 16;
   const int64_t qcs = (p.M + 1) / 2, scs = (p.M + 15) / 16;
 
-  auto tile_r0 = [&](int64_t t) { return (t % p.n_isteps) * T5_ROWS; };
-  auto tile_c0 = [&](int64_t t) { return (t / p.n_isteps) * T5_COLS; };
+  int buf = 0;
+  for (int64_t u = 0; u < ng * nh; ++u) {
+    const int64_t strip = T6_XCDS * (u / nh) + xcd;
+    if (strip >= nstrips) continue;  // uniform per workgroup
+    {
+      const int64_t trow = per_xcd * (u % nh) + jw;
+      if (trow >= ntrows) continue;  // uniform per workgroup
+      const int64_t r0 = trow * T6_ROWS, c0 = strip * T6_COLS;
 
-  float acol[8], scol[8];
-  auto fill_cols = [&](int64_t c0) {
+      // column amax / S_enc of the lane's 8 columns
+      float acol[8], scol[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float a = 0.0f;
+      for (int k = 0; k < 8; ++k) {
+        float a = 0.0f;
+        if constexpr (COLW) {
+          if (p.col_mode == 0) a = p.col_amax[0];
+          else if (p.col_mode == 1) a = p.col_amax[c0 + 8 * lane + k];
+          else a = p.col_amax[r0 + 16 * wv];
+        }
+        acol[k] = a;
+        scol[k] = COLW ? global_encode_scale(a, p.F) : 1.0f;
+      }
+      // row amax / S_enc of the wave's 16 rows
+      if constexpr (ROWW) {
+        if (lane < 16) {
+          const float a = (p.row_mode == 0) ? p.row_amax[0] : p.row_amax[r0 + 16 * wv + lane];
+          sm.ra[wv][lane] = a;
+          sm.rs[wv][lane] = global_encode_scale(a, p.F);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      uint32_t w[16][NW];
+      {
+        const __amdgpu_buffer_rsrc_t rx =
+            make_rsrc(x + (r0 + 16 * wv) * K + c0, (int64_t)16 * K * (int64_t)sizeof(T));
+        const uint32_t vo = (uint32_t)(8 * lane * sizeof(T));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) load_row_buf<T>(rx, vo, (uint32_t)i * rowbytes, w[i]);
+      }
+      StoreT6 st;
+      st.wv = wv;
+      st.lane = lane;
+      st.par = par;
+      st.qrs = (uint32_t)qrs;
+      st.sr = &sm.sr[buf][0][0];
+      st.qc = &sm.qc[buf][0][0];
+      st.sc = &sm.sc[buf][0][0];
+      if constexpr (ROWW) {
+        st.qr = make_rsrc(p.q_row + (r0 + 16 * wv) * qrs + c0 / 2, (int64_t)16 * qrs);
+        st.vo_qr = (uint32_t)(4 * lane);
+      }
+      process_block<T, ROWW, COLW>(w, st, 0, par, LdsTab{sm.ra[wv], sm.rs[wv], 0},
+                                   ColRegs{acol, scol}, p.F_inv);
+      __syncthreads();  // the tile's staged outputs are complete
+
+      if constexpr (ROWW) {  // 64 rows x 32 B: two lanes per row, 16 B each
+        if (tid < 2 * T6_ROWS) {
+          const int row = tid >> 1, half = tid & 1;
+          *reinterpret_cast<uint4*>(p.s_row + (r0 + row) * srs + c0 / 16 + 16 * half) =
+              *reinterpret_cast<const uint4*>(&sm.sr[buf][row][16 * half]);
+        }
+      }
       if constexpr (COLW) {
-        if (p.col_mode == 0) a = p.col_amax[0];
-        else if (p.col_mode == 1) a = p.col_amax[c0 + 8 * lane + k];
-      }
-      acol[k] = a;
-      scol[k] = COLW ? global_encode_scale(a, p.F) : 1.0f;
-    }
-  };
-  auto load_tile = [&](uint32_t (&wr)[16][NW], int64_t t) {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(
-        x + (tile_r0(t) + 16 * wv) * K + tile_c0(t), (int64_t)16 * K * (int64_t)sizeof(T));
-    const uint32_t vo = (uint32_t)(8 * lane * sizeof(T));
+        // 512 columns x 32 B: two lanes per column, 16 B each (wave slots
+        // restored to row order)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) load_row_buf<T>(rx, vo, (uint32_t)i * rowbytes, wr[i]);
-  };
-  // lanes 0..15: amax of row r0 + 16 wv + lane (issued one tile ahead)
-  auto load_row_amax = [&](int64_t t) -> float {
-    if constexpr (ROWW) {
-      if (lane < 16) return (p.row_mode == 0) ? p.row_amax[0] : p.row_amax[tile_r0(t) + 16 * wv + lane];
-    }
-    return 0.0f;
-  };
-
-  int64_t qc_r0 = tile_r0(t_begin), sc_r0 = qc_r0;  // first rows of the staged chunks
-  int sr_buf = 0;
-
-  auto run_tile = [&](const uint32_t (&wr)[16][NW], int64_t t, float a_mine) {
-    const int64_t r0 = tile_r0(t), c0 = tile_c0(t);
-    if constexpr (ROWW) {
-      if (lane < 16) {
-        sm.ra[wv][lane] = a_mine;
-        sm.rs[wv][lane] = global_encode_scale(a_mine, p.F);
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-    StoreT5 st;
-    st.wv = wv;
-    st.lane = lane;
-    st.par = par;
-    st.qrs = (uint32_t)qrs;
-    if constexpr (ROWW) {
-      st.qr = make_rsrc(p.q_row + (r0 + 16 * wv) * qrs + c0 / 2, (int64_t)16 * qrs);
-      st.vo_qr = (uint32_t)(4 * lane);
-      st.sr = &sm.sr[sr_buf][0][0];
-    }
-    if constexpr (COLW) {
-      st.qc = &sm.qc[(r0 - qc_r0) / T5_ROWS][0][0];
-      st.sc = &sm.sc[(r0 - sc_r0) / T5_ROWS][0][0];
-    }
-    const LdsTab rows{sm.ra[wv], sm.rs[wv], 0};
-    if (!COLW || p.col_mode == 1) {
-      process_block<T, ROWW, COLW>(wr, st, 0, par, rows, ColRegs{acol, scol}, p.F_inv);
-    } else {
-      UniformTab cols{0.0f, 1.0f};
-      cols.va = p.col_mode == 0 ? p.col_amax[0] : p.col_amax[r0 + 16 * wv];
-      cols.vs = global_encode_scale(cols.va, p.F);
-      process_block<T, ROWW, COLW>(wr, st, 0, par, rows, cols, p.F_inv);
-    }
-    __syncthreads();  // the tile's staged outputs are complete
-
-    // rowwise scales: 128 rows x 32 B, two threads per row, 16 B each
-    if constexpr (ROWW) {
-      if (tid < 2 * T5_ROWS) {
-        const int row = tid >> 1, half = tid & 1;
-        const uint4 v = *reinterpret_cast<const uint4*>(&sm.sr[sr_buf][row][16 * half]);
-        *reinterpret_cast<uint4*>(p.s_row + (r0 + row) * srs + c0 / 16 + 16 * half) = v;
-      }
-      sr_buf ^= 1;
-    }
-    if constexpr (COLW) {
-      const bool last = (t + 1 == t_end) || (tile_c0(t + 1) != c0);
-      const int64_t rows_end = r0 + T5_ROWS;
-      const bool flush_qc = last || (rows_end - qc_r0 == (int64_t)T5_QC_TILES * T5_ROWS);
-      const bool flush_sc = last || (rows_end - sc_r0 == (int64_t)T5_SC_TILES * T5_ROWS);
-      if (flush_qc) {
-        // 16-byte pieces, (tile, piece) fastest: 4 * nt pieces per column
-        const int nt = (int)((rows_end - qc_r0) / T5_ROWS);
-        const int per_col = 4 * nt;
-        for (int pidx = tid; pidx < T5_COLS * per_col; pidx += 512) {
-          const int c = pidx / per_col, pc = pidx - c * per_col;
-          const int h = pc >> 2, m = pc & 3;
-          const int xsw = (c >> 3) & 7;
-          const uint8_t* base = &sm.qc[h][c][0];
-          const uint2 lo = *reinterpret_cast<const uint2*>(base + 8 * ((2 * m) ^ xsw));
-          const uint2 hi = *reinterpret_cast<const uint2*>(base + 8 * ((2 * m + 1) ^ xsw));
-          *reinterpret_cast<uint4*>(p.q_col + (c0 + c) * qcs + qc_r0 / 2 + 64 * h + 16 * m) =
+        for (int it = 0; it < 4; ++it) {
+          const int pidx = tid + 256 * it;
+          const int c = pidx >> 1, half = pidx & 1;
+          const int xsw = (c >> 3) & 3;
+          const uint8_t* base = &sm.qc[buf][c][0];
+          const uint2 lo = *reinterpret_cast<const uint2*>(base + 8 * ((2 * half) ^ xsw));
+          const uint2 hi = *reinterpret_cast<const uint2*>(base + 8 * ((2 * half + 1) ^ xsw));
+          *reinterpret_cast<uint4*>(p.q_col + (c0 + c) * qcs + r0 / 2 + 16 * half) =
               make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
-        qc_r0 = rows_end;
-      }
-      if (flush_sc) {
-        // 8-byte pieces, tile fastest: nt pieces per column
-        const int nt = (int)((rows_end - sc_r0) / T5_ROWS);
-        for (int pidx = tid; pidx < T5_COLS * nt; pidx += 512) {
-          const int c = pidx / nt, sl = pidx - c * nt;
-          *reinterpret_cast<uint2*>(p.s_col + (c0 + c) * scs + sc_r0 / 16 + 8 * sl) =
-              *reinterpret_cast<const uint2*>(&sm.sc[sl][c][0]);
+        // 512 columns x 4 B
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int c = tid + 256 * it;
+          *reinterpret_cast<uint32_t*>(p.s_col + (c0 + c) * scs + r0 / 16) =
+              *reinterpret_cast<const uint32_t*>(&sm.sc[buf][c][0]);
         }
-        sc_r0 = rows_end;
       }
-      if (flush_qc || flush_sc) __syncthreads();  // stages free for the next tile
-      if (last && t + 1 < t_end) qc_r0 = sc_r0 = tile_r0(t + 1);
-    }
-  };
-
-  uint32_t wa[16][NW];
-  fill_cols(tile_c0(t_begin));
-  float am_a = load_row_amax(t_begin);
-  load_tile(wa, t_begin);
-  if constexpr (PREFETCH) {
-    uint32_t wb[16][NW];
-    for (int64_t t = t_begin; t < t_end; t += 2) {
-      float am_b = 0.0f;
-      if (t + 1 < t_end) {
-        am_b = load_row_amax(t + 1);
-        load_tile(wb, t + 1);
-      }
-      run_tile(wa, t, am_a);
-      if (t + 1 >= t_end) break;
-      if (tile_c0(t + 1) != tile_c0(t)) fill_cols(tile_c0(t + 1));
-      if (t + 2 < t_end) {
-        am_a = load_row_amax(t + 2);
-        load_tile(wa, t + 2);
-      }
-      run_tile(wb, t + 1, am_b);
-      if (t + 2 < t_end && tile_c0(t + 2) != tile_c0(t + 1)) fill_cols(tile_c0(t + 2));
-    }
-  } else {
-    for (int64_t t = t_begin; t < t_end; ++t) {
-      if (t > t_begin) {
-        if (tile_c0(t) != tile_c0(t - 1)) fill_cols(tile_c0(t));
-        am_a = load_row_amax(t);
-        load_tile(wa, t);
-      }
-      run_tile(wa, t, am_a);
+      buf ^= 1;
     }
   }
 }
@@ -650,27 +591,19 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
 }
 
 template <typename T, bool ROWW, bool COLW>
-static int interior_grid();
-
-// Whether the interior kernel keeps a second register buffer for the next tile.
-template <typename T>
-constexpr bool kPrefetch = false;
-
-template <typename T, bool ROWW, bool COLW>
 static int interior_grid() {
-  // resident workgroups per CU for the interior kernel, cached per device
+  // resident interior workgroups on the device (a multiple of 8), per device
   static int cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cache[dev] == 0) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW, kPrefetch<T>>),
-            512, 0) !=
+            &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW>), 256, 0) !=
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
-    cache[dev] = std::max(8, (num_cus() * std::min(per_cu, 1)) / 8 * 8);
+    cache[dev] = std::max(T6_XCDS, (num_cus() * per_cu) / T6_XCDS * T6_XCDS);
   }
   return cache[dev];
 }
@@ -680,9 +613,9 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
   const dim3 block(256);
   const int64_t ntiles = k.n_istrips * k.n_isteps;
   if (ntiles > 0) {
-    const int64_t G = std::min<int64_t>(interior_grid<T, ROWW, COLW>(), (ntiles + 7) / 8 * 8);
-    hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, kPrefetch<T>>), dim3((unsigned)G),
-                       dim3(512), 0, s, k);
+    const int64_t G = interior_grid<T, ROWW, COLW>();
+    hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW>), dim3((unsigned)G), dim3(256), 0, s,
+                       k);
   }
   // edge rectangles: (1) the partial last strip over all rows,
   // (2) the rows below the interior for the full strips
@@ -707,7 +640,7 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
   };
   const int64_t strips = (a.K + CAST_STRIP_COLS - 1) / CAST_STRIP_COLS;
   edge(0, a.M, k.n_istrips, strips - k.n_istrips);
-  edge(k.n_isteps * T5_ROWS, a.M, 0, k.n_istrips);
+  edge(k.n_isteps * T6_ROWS, a.M, 0, k.n_istrips);
 }
 
 template <typename T>
@@ -731,19 +664,19 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
   k.vec_load = ((a.K % V) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
   k.row_store4 = (a.K % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0);
   k.col_store8 = (a.M % 16 == 0) && ((reinterpret_cast<uintptr_t>(a.q_col) & 7) == 0);
-  // Interior (persistent, LDS-staged) path: 16-byte aligned rows, rows of
-  // every output aligned for its 16- or 8-byte stores (K % 256 == 0 for the
-  // rowwise scales, M % 128 == 0 for the transposed copy), and every in-tile
+  // Interior (persistent, super-step scheduled) path: 16-byte aligned rows
+  // and outputs aligned for their 16- and 4-byte stores (K % 256 == 0 for the
+  // rowwise scales, M % 64 == 0 for the transposed copy), and every in-tile
   // offset within 31 bits.
   const int64_t lim = 0x7FFFFFFF;
-  const bool fast = k.vec_load && (a.K % 256 == 0) && (a.M % T5_ROWS == 0) &&
+  const bool fast = k.vec_load && (a.K % 256 == 0) && (a.M % T6_ROWS == 0) &&
                     (!a.q_row || (reinterpret_cast<uintptr_t>(a.q_row) & 15) == 0) &&
                     (!a.s_row || (reinterpret_cast<uintptr_t>(a.s_row) & 15) == 0) &&
                     (!a.q_col || (reinterpret_cast<uintptr_t>(a.q_col) & 15) == 0) &&
                     (!a.s_col || (reinterpret_cast<uintptr_t>(a.s_col) & 7) == 0) &&
                     (int64_t)16 * a.K * (int64_t)sizeof(T) < lim;
-  k.n_istrips = fast ? a.K / T5_COLS : 0;
-  k.n_isteps = fast ? a.M / T5_ROWS : 0;
+  k.n_istrips = fast ? a.K / T6_COLS : 0;
+  k.n_isteps = fast ? a.M / T6_ROWS : 0;
   if (k.n_istrips == 0 || k.n_isteps == 0) k.n_istrips = k.n_isteps = 0;
   const bool rw = a.q_row != nullptr, cw = a.q_col != nullptr;
   if (rw && cw) launch_cast_kernels<T, true, true>(k, a, s);
