@@ -4,14 +4,9 @@
 // PR summary: the columnwise / transposed output is emitted in the same kernel
 // pass as the rowwise one, each direction with its own second-level amax).
 //
-// Geometry. A workgroup is 4 waves and owns a strip of 512 columns over a
-// segment of rows; it walks the segment 64 rows at a time. In one step lane
-// (wave w, DPP row g, lane-in-row q) holds a 16 x 8 register block of X:
-// rows r0 + 16g .. +16, columns c0 + 128w + 8q .. +8. Each 16-lane DPP row
-// loads 16 x 16 B of one row per BF16 load instruction (two for FP32), i.e.
-// whole 256-byte (512-byte) row segments: loads are coalesced and X is never
-// read column-strided. The transpose happens in registers:
-//   rowwise   -- a 16-element row block spans the lane pair (q, q^1); their
+// Geometry. A lane always works on a 16 x 8 register block of X (16 rows, 8
+// consecutive columns), which gives both directions without moving data:
+//   rowwise   -- a 16-element row block spans the lane pair (l, l^1); their
 //                8-element maxima meet through one DPP swap. The pair splits
 //                the 16 block-scale computations (even lane: even rows, odd
 //                lane: odd rows) and DPP broadcasts hand each row's encode
@@ -19,16 +14,14 @@
 //   columnwise-- each of the lane's 8 columns has all 16 rows of a column
 //                block in the lane itself: the block max is a register
 //                reduction (packed u16 max for BF16), no data exchange.
-// Stores: a DPP row writes 64 contiguous bytes of rowwise codes per row (the 4
-// waves of the workgroup fill 256 contiguous bytes); the 4 DPP rows of a wave
-// write 4 x 8 contiguous bytes of one transposed line, and the workgroup's
-// consecutive steps extend those lines, so partial lines meet in L2 before
-// they are written back.
+// Loads are whole row segments (16 bytes per lane, consecutive lanes on
+// consecutive columns), so X is never read column-strided.
 //
-// Interior workgroups (the whole strip inside K, whole 64-row steps, aligned
-// rows) use buffer loads and stores whose per-row offsets are uniform scalar
-// values, so addressing costs no vector ALU; edge workgroups take a checked
-// path with per-element bounds.
+// Two kernels share that block code. The interior kernel (persistent,
+// 256 x 256 macro tiles, buffer addressing with scalar row offsets, outputs
+// staged so that whole lines leave the workgroup) takes every tile of an
+// aligned shape; the edge kernel takes the rest with per-element bounds
+// checks.
 #include "nvfp4_device.h"
 #include "nvfp4_launch.h"
 
@@ -57,8 +50,8 @@ struct CastK {
   int vec_load;    // rows start 16-byte aligned
   int row_store4;  // K % 8 == 0: rowwise code rows are dword aligned
   int col_store8;  // M % 16 == 0: transposed code rows are 8-byte aligned
-  // interior kernel: tiles of 64 rows x 512 columns in the first n_isteps
-  // steps and n_istrips strips
+  // interior kernel: macro tiles of 256 rows x 256 columns, n_istrips strips
+  // by n_isteps macro rows
   int64_t n_istrips, n_isteps;
   // edge kernel: rows [rstart, rend) in segments of rows_per_wg (a multiple of
   // CAST_STEP_ROWS, <= CAST_MAX_ROWS_PER_WG); workgroup b takes segment
@@ -157,27 +150,6 @@ __device__ __forceinline__ void load_row_buf(__amdgpu_buffer_rsrc_t rx, uint32_t
 }
 
 // ------------------------------------------------------------------ stores
-// Interior: buffer stores, lane offsets fixed per workgroup, row / column
-// offsets uniform.
-struct StoreFast {
-  __amdgpu_buffer_rsrc_t qr, sr, qc, sc;
-  uint32_t vo_qr, vo_sr, vo_qc, vo_sc;  // per lane
-  uint32_t so_qr, so_sr, so_qc, so_sc;  // per step (uniform)
-  uint32_t qrs, srs, qcs, scs;
-  __device__ __forceinline__ void row_codes(int i, uint32_t word) const {
-    __builtin_amdgcn_raw_buffer_store_b32(word, qr, (int)vo_qr, (int)(so_qr + i * qrs), 0);
-  }
-  // the scale of row 2j + par of the lane pair's block
-  __device__ __forceinline__ void row_scale(int j, uint32_t byte) const {
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, sr, (int)vo_sr, (int)(so_sr + 2 * j * srs), 0);
-  }
-  __device__ __forceinline__ void col(int k, uint32_t w0, uint32_t w1, uint32_t byte) const {
-    const u32x2 v = {w0, w1};
-    __builtin_amdgcn_raw_buffer_store_b64(v, qc, (int)vo_qc, (int)(so_qc + k * qcs), 0);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, sc, (int)vo_sc, (int)(so_sc + k * scs), 0);
-  }
-};
-
 // Edge: global stores with bounds and alignment checks per element.
 struct StoreChecked {
   uint8_t *q_row, *s_row, *q_col, *s_col;
@@ -222,10 +194,16 @@ struct StoreChecked {
 //   col_a / col_s: amax and S_enc of the lane's 8 columns (index k)
 // Row pairs are encoded as soon as their block scales exist, so only the
 // data block and the 4-register running column max stay live.
-template <typename T, bool ROWW, bool COLW, class Store, class RowTab, class ColTab>
+struct NoMid {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+template <typename T, bool ROWW, bool COLW, class Store, class RowTab, class ColTab,
+          class Mid = NoMid>
 __device__ __forceinline__ void process_block(const uint32_t (&w)[16][Blk<T>::NW],
                                               const Store& st, int g, int par, const RowTab& row,
-                                              const ColTab& col, float f_inv) {
+                                              const ColTab& col, float f_inv,
+                                              const Mid& mid = Mid()) {
   constexpr int NW = Blk<T>::NW;
   uint32_t cm[NW];
 #pragma unroll
@@ -280,6 +258,8 @@ __device__ __forceinline__ void process_block(const uint32_t (&w)[16][Blk<T>::NW
     }
   }
 
+  mid();  // between the phases: the rows are no longer needed one by one
+
   if constexpr (COLW) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -333,58 +313,64 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 // --------------------------------------------------------- interior kernel
-// Interior tiles are 64 rows x 512 columns. A workgroup is 4 waves; wave w
-// holds rows r0 + 16w .. +16 of the tile and all 512 columns, lane l a 16 x 8
-// block at columns c0 + 8l, so every load instruction reads 1 KB of one row
-// and every rowwise-code store writes 256 contiguous bytes of one row.
+// Interior macro tiles are 256 rows x 256 columns, walked in two sub-steps of
+// 128 rows. A workgroup is 4 waves; in a sub-step wave w holds rows
+// rs + 32w .. +32 and lane (h = lane / 32, L = lane % 32) the 16 x 8 register
+// block at rows rs + 32w + 16h .. +16, columns c0 + 8L .. +8. A load
+// instruction reads 512 contiguous bytes of two rows (BF16).
 //
-// Schedule. On this GPU write bandwidth depends on how long the contiguous
-// runs that reach memory at about the same time are, far more than read
-// bandwidth does. The persistent workgroups therefore advance in lockstep
-// "super-steps": workgroup b runs on XCD x = b % 8 as its j = b / 8-th of
-// P = grid / 8 workgroups there, and in super-step u it takes strip
-// 8 * (u / nh) + x and tile row P * (u % nh) + j (nh = tile rows / P, rounded
-// up). At any moment the P (64 on MI355X) workgroups of an XCD cover P
-// consecutive tiles of one strip and the 8 XCDs cover 8 adjacent strips, so
-//   rowwise codes      -- one row gets 8 x 256 B = 2 KB in the same window
-//   transposed codes   -- one column gets 64 x 32 B = 2 KB, all from one XCD,
-//                         so its lines fill up in that XCD's L2
-//   scales             -- 256 B runs in both directions
-// Within a tile the transposed codes (32 B per column), transposed scales
-// (4 B per column) and rowwise scales (32 B per row) are gathered in LDS
-// (double buffered) and stored 16 bytes per lane where the run allows it.
-constexpr int T6_ROWS = 64;
-constexpr int T6_COLS = CAST_STRIP_COLS;  // 512
-constexpr int T6_XCDS = 8;
+// Why 256 x 256. On this GPU a store stream costs close to plain streaming
+// only when whole 128-byte lines leave the workgroup at once; partial lines
+// merge in the caches and their late write-back also slows whatever kernel
+// runs next. With 256 columns a rowwise-code row segment is 128 bytes, and
+// with 256 rows a transposed-code column segment is 128 bytes. Both are
+// written with non-temporal stores: rowwise codes straight from registers
+// (32 lanes x 4 bytes per row), transposed codes from LDS once the macro
+// tile is complete (8 lanes per column). The scales (16 bytes per row and per
+// column of the tile) take ordinary stores.
+//
+// Schedule. Workgroup b runs on XCD x = b % 8 as its j = b / 8-th of
+// P = grid / 8 workgroups there; its u-th macro tile is number t = u P + j of
+// the XCD's list, strip 8 (t / R) + x, macro row t % R (R = macro rows). The P
+// workgroups of an XCD therefore sweep whole strips together, and the 8 XCDs
+// work on adjacent strips.
+constexpr int IT_COLS = 256;                 // strip width
+constexpr int IT_SUB = 128;                  // rows per sub-step
+constexpr int IT_MACRO = 2 * IT_SUB;         // rows per macro tile
+constexpr int IT_XCDS = 8;
 
-struct T6Smem {
-  // transposed codes: [buf][column][4 waves x 8 B], wave w's slot at w ^ ((column >> 3) & 3)
-  uint8_t qc[2][T6_COLS][32];
-  // transposed scales: [buf][column][4 waves x 1 B]
-  uint8_t sc[2][T6_COLS][4];
-  // rowwise scales: [buf][row][32 B]
-  uint8_t sr[2][T6_ROWS][32];
-  // per-wave row amax / S_enc of the wave's 16 rows
-  float ra[4][16], rs[4][16];
+struct ITSmem {
+  // transposed codes of the macro tile, [buf][storage column][16 slots x 8 B].
+  // Slot s holds rows 16s .. +16 of the column. Column c is stored at
+  // c ^ ((c >> 3) & 1) and slot s at position s ^ ((c >> 3) & 15), so the 64
+  // lanes of one store instruction spread over all 64 banks.
+  uint8_t qc[2][IT_COLS][128];
+  // transposed scales, [buf][column][16 blocks]
+  uint8_t sc[2][IT_COLS][16];
+  // rowwise scales of a sub-step, [buf][row][16 blocks]
+  uint8_t sr[2][IT_SUB][16];
+  // per-wave row amax / S_enc of the wave's 32 rows
+  float ra[4][32], rs[4][32];
 };
 
-struct StoreT6 {
-  __amdgpu_buffer_rsrc_t qr;  // rowwise codes of this tile
+struct StoreIT {
+  __amdgpu_buffer_rsrc_t qr;  // rowwise codes of the wave's 32 rows
   uint32_t vo_qr, qrs;
   uint8_t* sr;
   uint8_t* qc;
   uint8_t* sc;
-  int wv, lane, par;
+  int wv, h, L, par, slot;
   __device__ __forceinline__ void row_codes(int i, uint32_t word) const {
-    __builtin_amdgcn_raw_buffer_store_b32(word, qr, (int)vo_qr, (int)(i * qrs), 0);
+    __builtin_amdgcn_raw_buffer_store_b32(word, qr, (int)vo_qr, (int)(i * qrs), 2 /* nt */);
   }
   __device__ __forceinline__ void row_scale(int j, uint32_t byte) const {
-    sr[(16 * wv + 2 * j + par) * 32 + (lane >> 1)] = (uint8_t)byte;
+    sr[(32 * wv + 16 * h + 2 * j + par) * 16 + (L >> 1)] = (uint8_t)byte;
   }
   __device__ __forceinline__ void col(int k, uint32_t w0, uint32_t w1, uint32_t byte) const {
-    const int c = 8 * lane + k;
-    *reinterpret_cast<uint2*>(qc + c * 32 + 8 * (wv ^ (lane & 3))) = make_uint2(w0, w1);
-    sc[c * 4 + wv] = (uint8_t)byte;
+    const int c = 8 * L + k;
+    const int pos = slot ^ (L & 15);
+    *reinterpret_cast<uint2*>(qc + (c ^ (L & 1)) * 128 + 8 * pos) = make_uint2(w0, w1);
+    sc[c * 16 + slot] = (uint8_t)byte;
   }
 };
 
@@ -392,111 +378,158 @@ template <typename T, bool ROWW, bool COLW>
 __global__ void __launch_bounds__(256) cast_interior_kernel(const CastK p) {
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   constexpr int NW = Blk<T>::NW;
-  __shared__ __attribute__((aligned(16))) T6Smem sm;
+  __shared__ __attribute__((aligned(16))) ITSmem sm;
   const T* __restrict__ x = static_cast<const T*>(p.x);
   const int tid = threadIdx.x;
-  const int wv = tid >> 6;
+  // The wave index is uniform across a wave; reading it into a scalar register
+  // keeps every buffer descriptor derived from it scalar (no per-lane loop
+  // around the buffer loads and stores).
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int par = lane & 1;
+  const int h = lane >> 5, L = lane & 31, par = lane & 1;
   const int64_t K = p.K;
 
-  const int64_t G = gridDim.x;  // T6_XCDS * per_xcd workgroups
-  const int64_t per_xcd = G / T6_XCDS;  // tiles of one strip an XCD covers per super-step
-  const int64_t xcd = blockIdx.x % T6_XCDS, jw = blockIdx.x / T6_XCDS;
-  const int64_t nstrips = p.n_istrips, ntrows = p.n_isteps;  // tile rows per strip
-  const int64_t nh = (ntrows + per_xcd - 1) / per_xcd;
-  const int64_t ng = (nstrips + T6_XCDS - 1) / T6_XCDS;
+  const int64_t per = gridDim.x / IT_XCDS;
+  const int64_t xcd = blockIdx.x % IT_XCDS, jw = blockIdx.x / IT_XCDS;
+  const int64_t nstrips = p.n_istrips, nmr = p.n_isteps;  // strips, macro rows
+  const int64_t ntiles_x = nmr * ((nstrips + IT_XCDS - 1) / IT_XCDS);  // per XCD
+  const int64_t n_v = 2 * ((ntiles_x + per - 1) / per);  // sub-steps scheduled
 
   const uint32_t rowbytes = (uint32_t)(K * (int64_t)sizeof(T));
   const int64_t qrs = (K + 1) / 2, srs = (K + 15) / 16;
   const int64_t qcs = (p.M + 1) / 2, scs = (p.M + 15) / 16;
 
-  int buf = 0;
-  for (int64_t u = 0; u < ng * nh; ++u) {
-    const int64_t strip = T6_XCDS * (u / nh) + xcd;
-    if (strip >= nstrips) continue;  // uniform per workgroup
-    {
-      const int64_t trow = per_xcd * (u % nh) + jw;
-      if (trow >= ntrows) continue;  // uniform per workgroup
-      const int64_t r0 = trow * T6_ROWS, c0 = strip * T6_COLS;
-
-      // column amax / S_enc of the lane's 8 columns
-      float acol[8], scol[8];
+  // sub-step v: macro tile origin (m0, c0); false when outside the interior
+  // (uniform per workgroup, the same for both sub-steps of a tile)
+  auto tile_of = [&](int64_t v, int64_t& m0, int64_t& c0) -> bool {
+    const int64_t t = (v >> 1) * per + jw;
+    const int64_t strip = IT_XCDS * (t / nmr) + xcd;
+    m0 = (t % nmr) * IT_MACRO;
+    c0 = strip * IT_COLS;
+    return t < ntiles_x && strip < nstrips;
+  };
+  auto next_sub = [&](int64_t v, int64_t& m0, int64_t& c0) -> int64_t {
+    while (v < n_v && !tile_of(v, m0, c0)) ++v;
+    return v;
+  };
+  const uint32_t vo = (uint32_t)h * 16u * rowbytes + (uint32_t)(8 * L * sizeof(T));
+  auto wave_rows = [&](int64_t rs, int64_t c0) {
+    return make_rsrc(x + (rs + 32 * wv) * K + c0, (int64_t)32 * K * (int64_t)sizeof(T));
+  };
+  // The first PF rows of each half of the wave's next sub-step are loaded while
+  // the current one's columnwise half runs (BF16: 32 registers; FP32 has none
+  // to spare).
+  constexpr int PF = sizeof(T) == 2 ? 8 : 0;
+  uint32_t pf[PF > 0 ? PF : 1][NW];
+  auto prefetch = [&](int64_t rs, int64_t c0) {
+    if constexpr (PF > 0) {
+      const __amdgpu_buffer_rsrc_t rn = wave_rows(rs, c0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        float a = 0.0f;
-        if constexpr (COLW) {
-          if (p.col_mode == 0) a = p.col_amax[0];
-          else if (p.col_mode == 1) a = p.col_amax[c0 + 8 * lane + k];
-          else a = p.col_amax[r0 + 16 * wv];
-        }
-        acol[k] = a;
-        scol[k] = COLW ? global_encode_scale(a, p.F) : 1.0f;
-      }
-      // row amax / S_enc of the wave's 16 rows
-      if constexpr (ROWW) {
-        if (lane < 16) {
-          const float a = (p.row_mode == 0) ? p.row_amax[0] : p.row_amax[r0 + 16 * wv + lane];
-          sm.ra[wv][lane] = a;
-          sm.rs[wv][lane] = global_encode_scale(a, p.F);
-        }
-        __builtin_amdgcn_wave_barrier();
-      }
-      uint32_t w[16][NW];
-      {
-        const __amdgpu_buffer_rsrc_t rx =
-            make_rsrc(x + (r0 + 16 * wv) * K + c0, (int64_t)16 * K * (int64_t)sizeof(T));
-        const uint32_t vo = (uint32_t)(8 * lane * sizeof(T));
-#pragma unroll
-        for (int i = 0; i < 16; ++i) load_row_buf<T>(rx, vo, (uint32_t)i * rowbytes, w[i]);
-      }
-      StoreT6 st;
-      st.wv = wv;
-      st.lane = lane;
-      st.par = par;
-      st.qrs = (uint32_t)qrs;
-      st.sr = &sm.sr[buf][0][0];
-      st.qc = &sm.qc[buf][0][0];
-      st.sc = &sm.sc[buf][0][0];
-      if constexpr (ROWW) {
-        st.qr = make_rsrc(p.q_row + (r0 + 16 * wv) * qrs + c0 / 2, (int64_t)16 * qrs);
-        st.vo_qr = (uint32_t)(4 * lane);
-      }
-      process_block<T, ROWW, COLW>(w, st, 0, par, LdsTab{sm.ra[wv], sm.rs[wv], 0},
-                                   ColRegs{acol, scol}, p.F_inv);
-      __syncthreads();  // the tile's staged outputs are complete
-
-      if constexpr (ROWW) {  // 64 rows x 32 B: two lanes per row, 16 B each
-        if (tid < 2 * T6_ROWS) {
-          const int row = tid >> 1, half = tid & 1;
-          *reinterpret_cast<uint4*>(p.s_row + (r0 + row) * srs + c0 / 16 + 16 * half) =
-              *reinterpret_cast<const uint4*>(&sm.sr[buf][row][16 * half]);
-        }
-      }
-      if constexpr (COLW) {
-        // 512 columns x 32 B: two lanes per column, 16 B each (wave slots
-        // restored to row order)
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int pidx = tid + 256 * it;
-          const int c = pidx >> 1, half = pidx & 1;
-          const int xsw = (c >> 3) & 3;
-          const uint8_t* base = &sm.qc[buf][c][0];
-          const uint2 lo = *reinterpret_cast<const uint2*>(base + 8 * ((2 * half) ^ xsw));
-          const uint2 hi = *reinterpret_cast<const uint2*>(base + 8 * ((2 * half + 1) ^ xsw));
-          *reinterpret_cast<uint4*>(p.q_col + (c0 + c) * qcs + r0 / 2 + 16 * half) =
-              make_uint4(lo.x, lo.y, hi.x, hi.y);
-        }
-        // 512 columns x 4 B
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-          const int c = tid + 256 * it;
-          *reinterpret_cast<uint32_t*>(p.s_col + (c0 + c) * scs + r0 / 16) =
-              *reinterpret_cast<const uint32_t*>(&sm.sc[buf][c][0]);
-        }
-      }
-      buf ^= 1;
+      for (int i = 0; i < PF; ++i) load_row_buf<T>(rn, vo, (uint32_t)i * rowbytes, pf[i]);
     }
+  };
+
+  int sbuf = 0, mbuf = 0;
+  int64_t m0 = 0, c0 = 0;
+  int64_t v = next_sub(0, m0, c0);
+  if (v < n_v) prefetch(m0 + (v & 1) * IT_SUB, c0);
+  while (v < n_v) {
+    const int sub = (int)(v & 1);
+    const int64_t rs = m0 + sub * IT_SUB;
+    // column amax / S_enc of the lane's 8 columns (mode 2: the group amax of
+    // the lane's 16-row block)
+    float acol[8], scol[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float a = 0.0f;
+      if constexpr (COLW) {
+        if (p.col_mode == 0) a = p.col_amax[0];
+        else if (p.col_mode == 1) a = p.col_amax[c0 + 8 * L + k];
+        else a = p.col_amax[rs + 32 * wv + 16 * h];
+      }
+      acol[k] = a;
+      scol[k] = COLW ? global_encode_scale(a, p.F) : 1.0f;
+    }
+    // row amax / S_enc of the wave's 32 rows
+    if constexpr (ROWW) {
+      if (lane < 32) {
+        const float a = (p.row_mode == 0) ? p.row_amax[0] : p.row_amax[rs + 32 * wv + lane];
+        sm.ra[wv][lane] = a;
+        sm.rs[wv][lane] = global_encode_scale(a, p.F);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    uint32_t w[16][NW];
+    {
+      const __amdgpu_buffer_rsrc_t rx = wave_rows(rs, c0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < PF) {
+#pragma unroll
+          for (int d = 0; d < NW; ++d) w[i][d] = pf[i < PF ? i : 0][d];
+        } else {
+          load_row_buf<T>(rx, vo, (uint32_t)i * rowbytes, w[i]);
+        }
+      }
+    }
+    int64_t m0n = 0, c0n = 0;
+    const int64_t vn = next_sub(v + 1, m0n, c0n);
+
+    StoreIT st;
+    st.wv = wv;
+    st.h = h;
+    st.L = L;
+    st.par = par;
+    st.slot = 8 * sub + 2 * wv + h;
+    st.qrs = (uint32_t)qrs;
+    st.sr = &sm.sr[sbuf][0][0];
+    st.qc = &sm.qc[mbuf][0][0];
+    st.sc = &sm.sc[mbuf][0][0];
+    if constexpr (ROWW) {
+      st.qr = make_rsrc(p.q_row + (rs + 32 * wv) * qrs + c0 / 2, (int64_t)32 * qrs);
+      st.vo_qr = (uint32_t)h * 16u * (uint32_t)qrs + (uint32_t)(4 * L);
+    }
+    auto mid = [&]() {
+      if (vn < n_v) prefetch(m0n + (vn & 1) * IT_SUB, c0n);
+    };
+    process_block<T, ROWW, COLW>(w, st, h, par, LdsTab{sm.ra[wv], sm.rs[wv], 0},
+                                 ColRegs{acol, scol}, p.F_inv, mid);
+    __syncthreads();  // the sub-step's staged outputs are complete
+
+    if constexpr (ROWW) {  // 128 rows x 16 B
+      if (tid < IT_SUB)
+        *reinterpret_cast<uint4*>(p.s_row + (rs + tid) * srs + c0 / 16) =
+            *reinterpret_cast<const uint4*>(&sm.sr[sbuf][tid][0]);
+    }
+    sbuf ^= 1;
+    if (COLW && sub == 1) {
+      // 256 columns x 128 B of transposed codes: 8 lanes per column, whole
+      // lines, slots restored to row order
+#pragma unroll
+      for (int it = 0; it < IT_COLS * 8 / 256; ++it) {
+        const int pidx = tid + 256 * it;
+        const int c = pidx >> 3, t = pidx & 7;
+        const int f = (c >> 3) & 15;
+        u32x4 q = *reinterpret_cast<const u32x4*>(&sm.qc[mbuf][c ^ (f & 1)][16 * (t ^ (f >> 1))]);
+        if (f & 1) q = (u32x4){q.z, q.w, q.x, q.y};
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p.q_col + (c0 + c) * qcs + m0 / 2 + 16 * t));
+      }
+      // 256 columns x 16 B of transposed scales
+      {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(&sm.sc[mbuf][tid][0]);
+        uint8_t* dst = p.s_col + (c0 + tid) * scs + m0 / 16;
+        if ((scs & 15) == 0) {
+          *reinterpret_cast<u32x4*>(dst) = q;
+        } else {
+          uint32_t* d4 = reinterpret_cast<uint32_t*>(dst);
+          d4[0] = q.x; d4[1] = q.y; d4[2] = q.z; d4[3] = q.w;
+        }
+      }
+      mbuf ^= 1;
+    }
+    v = vn;
+    m0 = m0n;
+    c0 = c0n;
   }
 }
 
@@ -603,7 +636,7 @@ static int interior_grid() {
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
-    cache[dev] = std::max(T6_XCDS, (num_cus() * per_cu) / T6_XCDS * T6_XCDS);
+    cache[dev] = std::max(IT_XCDS, (num_cus() * per_cu) / IT_XCDS * IT_XCDS);
   }
   return cache[dev];
 }
@@ -639,8 +672,10 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
                        0, s, k);
   };
   const int64_t strips = (a.K + CAST_STRIP_COLS - 1) / CAST_STRIP_COLS;
-  edge(0, a.M, k.n_istrips, strips - k.n_istrips);
-  edge(k.n_isteps * T6_ROWS, a.M, 0, k.n_istrips);
+  if (ntiles > 0)  // the interior spans every column: the rows below it remain
+    edge(k.n_isteps * IT_MACRO, a.M, 0, strips);
+  else
+    edge(0, a.M, 0, strips);
 }
 
 template <typename T>
@@ -664,19 +699,22 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
   k.vec_load = ((a.K % V) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
   k.row_store4 = (a.K % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0);
   k.col_store8 = (a.M % 16 == 0) && ((reinterpret_cast<uintptr_t>(a.q_col) & 7) == 0);
-  // Interior (persistent, super-step scheduled) path: 16-byte aligned rows
-  // and outputs aligned for their 16- and 4-byte stores (K % 256 == 0 for the
-  // rowwise scales, M % 64 == 0 for the transposed copy), and every in-tile
-  // offset within 31 bits.
+  // Interior (persistent macro-tile) path: 16-byte aligned rows, K % 256 == 0
+  // (whole strips; 16-byte rowwise-scale stores), M % 64 == 0 (16-byte
+  // transposed-code stores, at least 4-byte transposed-scale stores), outputs
+  // aligned for those stores, and every in-tile offset within 31 bits. Rows
+  // below the last whole macro tile go to the edge kernel.
   const int64_t lim = 0x7FFFFFFF;
-  const bool fast = k.vec_load && (a.K % 256 == 0) && (a.M % T6_ROWS == 0) &&
-                    (!a.q_row || (reinterpret_cast<uintptr_t>(a.q_row) & 15) == 0) &&
+  const int64_t scs = (a.M + 15) / 16;
+  const uintptr_t sc_align = (scs % 16 == 0) ? 15 : 3;
+  const bool fast = k.vec_load && (a.K % IT_COLS == 0) && (a.M % 64 == 0) &&
+                    (!a.q_row || (reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0) &&
                     (!a.s_row || (reinterpret_cast<uintptr_t>(a.s_row) & 15) == 0) &&
                     (!a.q_col || (reinterpret_cast<uintptr_t>(a.q_col) & 15) == 0) &&
-                    (!a.s_col || (reinterpret_cast<uintptr_t>(a.s_col) & 7) == 0) &&
-                    (int64_t)16 * a.K * (int64_t)sizeof(T) < lim;
-  k.n_istrips = fast ? a.K / T6_COLS : 0;
-  k.n_isteps = fast ? a.M / T6_ROWS : 0;
+                    (!a.s_col || (reinterpret_cast<uintptr_t>(a.s_col) & sc_align) == 0) &&
+                    (int64_t)32 * a.K * (int64_t)sizeof(T) < lim;
+  k.n_istrips = fast ? a.K / IT_COLS : 0;
+  k.n_isteps = fast ? a.M / IT_MACRO : 0;
   if (k.n_istrips == 0 || k.n_isteps == 0) k.n_istrips = k.n_isteps = 0;
   const bool rw = a.q_row != nullptr, cw = a.q_col != nullptr;
   if (rw && cw) launch_cast_kernels<T, true, true>(k, a, s);
