@@ -285,6 +285,123 @@ __device__ __forceinline__ void process_block(const uint32_t (&w)[16][Blk<T>::NW
   }
 }
 
+// Two E2M1 codes into byte `sel` (a constant after unrolling) of `old`.
+__device__ __forceinline__ uint32_t cvt_fp4x2_sel(uint32_t old, float v0, float v1, int sel) {
+  switch (sel & 3) {
+    case 0: return NVFP4_CVT_FP4X2(old, v0, v1, 0);
+    case 1: return NVFP4_CVT_FP4X2(old, v0, v1, 1);
+    case 2: return NVFP4_CVT_FP4X2(old, v0, v1, 2);
+    default: return NVFP4_CVT_FP4X2(old, v0, v1, 3);
+  }
+}
+
+// The same two directions as process_block, in three batched phases, so that
+// independent work sits side by side for the scheduler:
+//   1. every block maximum of the 16 x 8 block (integer max on magnitudes);
+//   2. all 16 block scales (8 row blocks shared with the lane pair, 8 column
+//      blocks) -- 16 independent dependency chains;
+//   3. every element converted to fp32 once, multiplied by its row and its
+//      column encode factor, both products converted to E2M1.
+// `mid` runs after phase 1 (the next tile's loads can be issued there).
+template <typename T, bool ROWW, bool COLW, class Store, class RowTab, class ColTab, class Mid>
+__device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Blk<T>::NW],
+                                                      const Store& st, int g, int par,
+                                                      const RowTab& row, const ColTab& col,
+                                                      float f_inv, const Mid& mid) {
+  constexpr int NW = Blk<T>::NW;
+  // ---- phase 1: maxima
+  uint32_t cm[NW];
+  uint32_t rb[16];
+#pragma unroll
+  for (int d = 0; d < NW; ++d) cm[d] = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t a0 = w[i][0] & kAbsBf16x2, a1 = w[i][1] & kAbsBf16x2;
+      const uint32_t a2 = w[i][2] & kAbsBf16x2, a3 = w[i][3] & kAbsBf16x2;
+      if constexpr (COLW) {
+        cm[0] = pk_max_u16(cm[0], a0);
+        cm[1] = pk_max_u16(cm[1], a1);
+        cm[2] = pk_max_u16(cm[2], a2);
+        cm[3] = pk_max_u16(cm[3], a3);
+      }
+      if constexpr (ROWW) {
+        const uint32_t t = pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3));
+        rb[i] = max(t & 0xFFFFu, t >> 16) << 16;
+      }
+    } else {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t av = w[i][k] & kAbsF32;
+        if constexpr (COLW) cm[k] = max(cm[k], av);
+        m = max(m, av);
+      }
+      rb[i] = m;
+    }
+  }
+  mid();
+
+  // ---- phase 2: scales
+  float renc[8];  // encode factor of this lane's row 2j + par
+  if constexpr (ROWW) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t b0 = max(rb[2 * j], dpp_swap1(rb[2 * j]));
+      const uint32_t b1 = max(rb[2 * j + 1], dpp_swap1(rb[2 * j + 1]));
+      const uint32_t bsel = par ? b1 : b0;
+      const int lr = 16 * g + 2 * j + par;
+      uint32_t byte;
+      block_scale(__uint_as_float(bsel), row.a(lr), row.s(lr), f_inv, &byte, &renc[j]);
+      st.row_scale(j, byte);
+    }
+  }
+  float cenc[8];
+  if constexpr (COLW) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      uint32_t cb;
+      if constexpr (sizeof(T) == 2)
+        cb = (k & 1) ? (cm[k >> 1] & 0xFFFF0000u) : (cm[k >> 1] << 16);
+      else
+        cb = cm[k];
+      uint32_t byte;
+      block_scale(__uint_as_float(cb), col.a(k), col.s(k), f_inv, &byte, &cenc[k]);
+      st.col_scale(k, byte);
+    }
+  }
+
+  // ---- phase 3: codes
+  uint32_t cc[8][2];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) cc[k][0] = cc[k][1] = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float xv[2][8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) xv[e][k] = elem<T>(w, 2 * j + e, k);
+    if constexpr (ROWW) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float r = e ? bcast_odd(renc[j]) : bcast_even(renc[j]);
+        st.row_codes(2 * j + e, e2m1_pack8(xv[e][0] * r, xv[e][1] * r, xv[e][2] * r, xv[e][3] * r,
+                                           xv[e][4] * r, xv[e][5] * r, xv[e][6] * r, xv[e][7] * r));
+      }
+    }
+    if constexpr (COLW) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        cc[k][j >> 2] = cvt_fp4x2_sel(cc[k][j >> 2], xv[0][k] * cenc[k], xv[1][k] * cenc[k], j);
+    }
+  }
+  if constexpr (COLW) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st.col_codes(k, cc[k][0], cc[k][1]);
+  }
+}
+
 // Row / column tables in LDS (a pointer and a base index).
 struct LdsTab {
   const float* pa;
@@ -299,6 +416,15 @@ struct ColRegs {
   const float (&vs)[8];
   __device__ __forceinline__ float a(int k) const { return va[k]; }
   __device__ __forceinline__ float s(int k) const { return vs[k]; }
+};
+// The lane's 8 columns from an LDS table, or one value for all of them.
+struct ColSel {
+  const float* pa;
+  const float* ps;
+  float ua, us;
+  bool uni;
+  __device__ __forceinline__ float a(int k) const { return uni ? ua : pa[k]; }
+  __device__ __forceinline__ float s(int k) const { return uni ? us : ps[k]; }
 };
 // One value for every entry (per-tensor / group amax modes).
 struct UniformTab {
@@ -351,6 +477,8 @@ struct ITSmem {
   uint8_t sr[2][IT_SUB][16];
   // per-wave row amax / S_enc of the wave's 32 rows
   float ra[4][32], rs[4][32];
+  // column amax / S_enc of the strip's 256 columns
+  float ca[IT_COLS], cs[IT_COLS];
 };
 
 struct StoreIT {
@@ -366,16 +494,18 @@ struct StoreIT {
   __device__ __forceinline__ void row_scale(int j, uint32_t byte) const {
     sr[(32 * wv + 16 * h + 2 * j + par) * 16 + (L >> 1)] = (uint8_t)byte;
   }
-  __device__ __forceinline__ void col(int k, uint32_t w0, uint32_t w1, uint32_t byte) const {
+  __device__ __forceinline__ void col_codes(int k, uint32_t w0, uint32_t w1) const {
     const int c = 8 * L + k;
     const int pos = slot ^ (L & 15);
     *reinterpret_cast<uint2*>(qc + (c ^ (L & 1)) * 128 + 8 * pos) = make_uint2(w0, w1);
-    sc[c * 16 + slot] = (uint8_t)byte;
+  }
+  __device__ __forceinline__ void col_scale(int k, uint32_t byte) const {
+    sc[(8 * L + k) * 16 + slot] = (uint8_t)byte;
   }
 };
 
 template <typename T, bool ROWW, bool COLW>
-__global__ void __launch_bounds__(256) cast_interior_kernel(const CastK p) {
+__global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_kernel(const CastK p) {
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   constexpr int NW = Blk<T>::NW;
   __shared__ __attribute__((aligned(16))) ITSmem sm;
@@ -430,25 +560,29 @@ __global__ void __launch_bounds__(256) cast_interior_kernel(const CastK p) {
   };
 
   int sbuf = 0, mbuf = 0;
-  int64_t m0 = 0, c0 = 0;
+  int64_t m0 = 0, c0 = 0, c0_tab = -1;
   int64_t v = next_sub(0, m0, c0);
   if (v < n_v) prefetch(m0 + (v & 1) * IT_SUB, c0);
   while (v < n_v) {
     const int sub = (int)(v & 1);
     const int64_t rs = m0 + sub * IT_SUB;
-    // column amax / S_enc of the lane's 8 columns (mode 2: the group amax of
-    // the lane's 16-row block)
-    float acol[8], scol[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float a = 0.0f;
-      if constexpr (COLW) {
-        if (p.col_mode == 0) a = p.col_amax[0];
-        else if (p.col_mode == 1) a = p.col_amax[c0 + 8 * L + k];
-        else a = p.col_amax[rs + 32 * wv + 16 * h];
+    // column amax / S_enc: the strip's table in LDS (modes 0 and 1, filled
+    // when the strip changes), or the group amax of the lane's 16-row block
+    // (mode 2)
+    ColSel ctab{&sm.ca[8 * L], &sm.cs[8 * L], 0.0f, 1.0f, false};
+    if constexpr (COLW) {
+      if (p.col_mode == 2) {
+        ctab.uni = true;
+        ctab.ua = p.col_amax[rs + 32 * wv + 16 * h];
+        ctab.us = global_encode_scale(ctab.ua, p.F);
+      } else if (c0 != c0_tab) {
+        const float a = p.col_amax[p.col_mode == 0 ? 0 : c0 + tid];
+        __syncthreads();  // every wave is done with the previous strip's table
+        sm.ca[tid] = a;
+        sm.cs[tid] = global_encode_scale(a, p.F);
+        __syncthreads();
+        c0_tab = c0;
       }
-      acol[k] = a;
-      scol[k] = COLW ? global_encode_scale(a, p.F) : 1.0f;
     }
     // row amax / S_enc of the wave's 32 rows
     if constexpr (ROWW) {
@@ -492,8 +626,8 @@ __global__ void __launch_bounds__(256) cast_interior_kernel(const CastK p) {
     auto mid = [&]() {
       if (vn < n_v) prefetch(m0n + (vn & 1) * IT_SUB, c0n);
     };
-    process_block<T, ROWW, COLW>(w, st, h, par, LdsTab{sm.ra[wv], sm.rs[wv], 0},
-                                 ColRegs{acol, scol}, p.F_inv, mid);
+    process_block_batched<T, ROWW, COLW>(w, st, h, par, LdsTab{sm.ra[wv], sm.rs[wv], 0}, ctab,
+                                         p.F_inv, mid);
     __syncthreads();  // the sub-step's staged outputs are complete
 
     if constexpr (ROWW) {  // 128 rows x 16 B
