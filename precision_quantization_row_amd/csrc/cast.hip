@@ -138,13 +138,15 @@ __device__ __forceinline__ void load_row_checked(const T* __restrict__ x, int64_
   }
 }
 
+// X is read once by this pass: non-temporal loads keep it from displacing the
+// partially written scale lines that are still merging in L2.
 template <typename T>
 __device__ __forceinline__ void load_row_buf(__amdgpu_buffer_rsrc_t rx, uint32_t vo, uint32_t so,
                                              uint32_t (&out)[Blk<T>::NW]) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)vo, (int)so, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)vo, (int)so, 2 /* nt */);
   out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
   if constexpr (sizeof(T) == 4) {
-    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(vo + 16u), (int)so, 0);
+    const u32x4 u = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(vo + 16u), (int)so, 2 /* nt */);
     out[4] = u.x; out[5] = u.y; out[6] = u.z; out[7] = u.w;
   }
 }
@@ -456,10 +458,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // column of the tile) take ordinary stores.
 //
 // Schedule. Workgroup b runs on XCD x = b % 8 as its j = b / 8-th of
-// P = grid / 8 workgroups there; its u-th macro tile is number t = u P + j of
-// the XCD's list, strip 8 (t / R) + x, macro row t % R (R = macro rows). The P
-// workgroups of an XCD therefore sweep whole strips together, and the 8 XCDs
-// work on adjacent strips.
+// P = grid / 8 workgroups there. XCD x owns the S = ceil(strips / 8)
+// consecutive strips x S .. x S + S - 1; the workgroup's u-th macro tile is
+// number t = u P + j of the XCD's list, strip x S + t / R, macro row t % R
+// (R = macro rows). The P workgroups of an XCD sweep whole strips together, so
+// a column's transposed scales (16 bytes per macro tile) and a row's rowwise
+// scales (16 bytes per strip) are completed within that XCD's L2 before they
+// are written back.
 constexpr int IT_COLS = 256;                 // strip width
 constexpr int IT_SUB = 128;                  // rows per sub-step
 constexpr int IT_MACRO = 2 * IT_SUB;         // rows per macro tile
@@ -522,7 +527,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
   const int64_t per = gridDim.x / IT_XCDS;
   const int64_t xcd = blockIdx.x % IT_XCDS, jw = blockIdx.x / IT_XCDS;
   const int64_t nstrips = p.n_istrips, nmr = p.n_isteps;  // strips, macro rows
-  const int64_t ntiles_x = nmr * ((nstrips + IT_XCDS - 1) / IT_XCDS);  // per XCD
+  const int64_t spx = (nstrips + IT_XCDS - 1) / IT_XCDS;  // strips per XCD
+  const int64_t ntiles_x = nmr * spx;                     // macro tiles per XCD
   const int64_t n_v = 2 * ((ntiles_x + per - 1) / per);  // sub-steps scheduled
 
   const uint32_t rowbytes = (uint32_t)(K * (int64_t)sizeof(T));
@@ -533,7 +539,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
   // (uniform per workgroup, the same for both sub-steps of a tile)
   auto tile_of = [&](int64_t v, int64_t& m0, int64_t& c0) -> bool {
     const int64_t t = (v >> 1) * per + jw;
-    const int64_t strip = IT_XCDS * (t / nmr) + xcd;
+    const int64_t strip = xcd * spx + t / nmr;
     m0 = (t % nmr) * IT_MACRO;
     c0 = strip * IT_COLS;
     return t < ntiles_x && strip < nstrips;
