@@ -137,6 +137,28 @@ def test_dequant_random_codes_all_bytes():
                     oracle_dequant_bits(q.numpy(), s.numpy(), R, C, 1, a.numpy(), 448.0, od))
 
 
+@pytest.mark.parametrize("R,C,shift", [(33, 4112, 0), (33, 4112, 1), (19, 150, 0), (5, 2064, 0)])
+@pytest.mark.parametrize("od", [torch.bfloat16, torch.float32])
+def test_dequant_signed_scales_chunks_and_alignment(R, C, shift, od):
+    """Scale bytes with the sign bit set decode to negative scales; lines that
+    span several vector chunks with a ragged last one (C = 4112, 2064), an
+    output that starts off a 16-byte boundary (shift = 1 element: the general
+    kernel) and a line length that is not a whole number of blocks (C = 150)."""
+    g = torch.Generator().manual_seed(11 + R + C + shift)
+    qrs, nb = (C + 1) // 2, (C + 15) // 16
+    q = torch.randint(0, 256, (R, qrs), generator=g, dtype=torch.uint8)
+    s = torch.randint(0, 127, (R, nb), generator=g, dtype=torch.uint8)
+    s = torch.where(torch.rand(R, nb, generator=g) < 0.5, s, s | 0x80)  # 0x80..0xFE
+    a = (torch.rand(R, generator=g) * 100).float()
+    dev = torch.device("cuda:0")
+    say(f"[gpu] dequant signed scales {R}x{C} shift={shift} {od}")
+    base = torch.empty(R * C + 8, dtype=od, device=dev)
+    y = base[shift:shift + R * C].view(R, C)
+    p.nvfp4_dequantize(q.to(dev), s.to(dev), R, C, p.NVFP4_AMAX_LINE, a.to(dev), 448.0, y)
+    assert_same(f"dequant {od}", dequant_bits(y.clone()),
+                oracle_dequant_bits(q.numpy(), s.numpy(), R, C, 1, a.numpy(), 448.0, od))
+
+
 # ---------------------------------------------------------------- noop
 def test_noop_leaves_every_buffer_untouched():
     """Fused-amax PR review: a call skipped by noop must not erase the
