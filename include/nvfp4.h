@@ -136,7 +136,11 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
  *   q [R][ceil(C/2)], sc [R][ceil(C/16)]: a rowwise copy (R = M, C = K) or a
  *       columnwise copy (R = K, C = M)
  *   amax_mode / amax: TENSOR ([1]), LINE ([R]) or ROWGROUP ([C])
- *   y [R][C] of out_dtype (NVFP4_BF16 or NVFP4_FP32). */
+ *   y [R][C] of out_dtype (NVFP4_BF16 or NVFP4_FP32).
+ * Scale bytes are E4M3FN values as nvfp4_quantize_transpose writes them
+ * (0x00-0x7E); a byte with the sign bit set decodes to the negative scale.
+ * 0x7F and 0xFF are the format's NaN encodings and are outside the contract
+ * (the output for their blocks is unspecified). */
 int nvfp4_dequantize(const uint8_t* q, const uint8_t* sc, int64_t R, int64_t C, int amax_mode,
                      const float* amax, float bound, void* y, int out_dtype, const float* noop,
                      void* stream);
