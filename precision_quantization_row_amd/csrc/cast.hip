@@ -476,7 +476,7 @@ struct ITSmem {
   // c ^ ((c >> 3) & 1) and slot s at position s ^ ((c >> 3) & 15), so the 64
   // lanes of one store instruction spread over all 64 banks.
   uint8_t qc[2][IT_COLS][128];
-  // transposed scales, [buf][column][16 blocks]
+  // transposed scales, [buf][entry][16 blocks]; column 8L + k at entry 32k + L
   uint8_t sc[2][IT_COLS][16];
   // rowwise scales of a sub-step, [buf][row][16 blocks]
   uint8_t sr[2][IT_SUB][16];
@@ -504,8 +504,10 @@ struct StoreIT {
     const int pos = slot ^ (L & 15);
     *reinterpret_cast<uint2*>(qc + (c ^ (L & 1)) * 128 + 8 * pos) = make_uint2(w0, w1);
   }
+  // column 8L + k is stored at entry 32k + L, so the lanes of one write land
+  // in different banks
   __device__ __forceinline__ void col_scale(int k, uint32_t byte) const {
-    sc[(8 * L + k) * 16 + slot] = (uint8_t)byte;
+    sc[(32 * k + L) * 16 + slot] = (uint8_t)byte;
   }
 };
 
@@ -654,10 +656,12 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
         if (f & 1) q = (u32x4){q.z, q.w, q.x, q.y};
         __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(p.q_col + (c0 + c) * qcs + m0 / 2 + 16 * t));
       }
-      // 256 columns x 16 B of transposed scales
+      // 256 columns x 16 B of transposed scales (entry tid holds column
+      // 8 (tid % 32) + tid / 32)
       {
         const u32x4 q = *reinterpret_cast<const u32x4*>(&sm.sc[mbuf][tid][0]);
-        uint8_t* dst = p.s_col + (c0 + tid) * scs + m0 / 16;
+        const int c = 8 * (tid & 31) + (tid >> 5);
+        uint8_t* dst = p.s_col + (c0 + c) * scs + m0 / 16;
         if ((scs & 15) == 0) {
           *reinterpret_cast<u32x4*>(dst) = q;
         } else {
