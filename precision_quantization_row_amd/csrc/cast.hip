@@ -344,32 +344,57 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
   }
   mid();
 
-  // ---- phase 2: scales
+  // ---- phase 2: scales. All 16 take the unguarded fast form; a lane where
+  // any of them falls outside its range (tiny blocks, extreme decode scales)
+  // redoes all of its scales with the guarded form.
   float renc[8];  // encode factor of this lane's row 2j + par
+  uint32_t bsel[8];
+  bool ok = true;
   if constexpr (ROWW) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t b0 = max(rb[2 * j], dpp_swap1(rb[2 * j]));
       const uint32_t b1 = max(rb[2 * j + 1], dpp_swap1(rb[2 * j + 1]));
-      const uint32_t bsel = par ? b1 : b0;
+      bsel[j] = par ? b1 : b0;
       const int lr = 16 * g + 2 * j + par;
       uint32_t byte;
-      block_scale(__uint_as_float(bsel), row.a(lr), row.s(lr), f_inv, &byte, &renc[j]);
+      ok &= block_scale_fast(__uint_as_float(bsel[j]), row.a(lr), row.s(lr), f_inv, &byte, &renc[j]);
       st.row_scale(j, byte);
     }
   }
   float cenc[8];
+  auto col_bits = [&](int k) -> uint32_t {
+    if constexpr (sizeof(T) == 2)
+      return (k & 1) ? (cm[k >> 1] & 0xFFFF0000u) : (cm[k >> 1] << 16);
+    else
+      return cm[k];
+  };
   if constexpr (COLW) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      uint32_t cb;
-      if constexpr (sizeof(T) == 2)
-        cb = (k & 1) ? (cm[k >> 1] & 0xFFFF0000u) : (cm[k >> 1] << 16);
-      else
-        cb = cm[k];
       uint32_t byte;
-      block_scale(__uint_as_float(cb), col.a(k), col.s(k), f_inv, &byte, &cenc[k]);
+      ok &= block_scale_fast(__uint_as_float(col_bits(k)), col.a(k), col.s(k), f_inv, &byte,
+                             &cenc[k]);
       st.col_scale(k, byte);
+    }
+  }
+  if (!ok) {
+    if constexpr (ROWW) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int lr = 16 * g + 2 * j + par;
+        uint32_t byte;
+        block_scale(__uint_as_float(bsel[j]), row.a(lr), row.s(lr), f_inv, &byte, &renc[j]);
+        st.row_scale(j, byte);
+      }
+    }
+    if constexpr (COLW) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        uint32_t byte;
+        block_scale(__uint_as_float(col_bits(k)), col.a(k), col.s(k), f_inv, &byte, &cenc[k]);
+        st.col_scale(k, byte);
+      }
     }
   }
 
@@ -419,14 +444,12 @@ struct ColRegs {
   __device__ __forceinline__ float a(int k) const { return va[k]; }
   __device__ __forceinline__ float s(int k) const { return vs[k]; }
 };
-// The lane's 8 columns from an LDS table, or one value for all of them.
-struct ColSel {
+// The lane's 8 columns, read from LDS (8 consecutive entries).
+struct ColLds {
   const float* pa;
   const float* ps;
-  float ua, us;
-  bool uni;
-  __device__ __forceinline__ float a(int k) const { return uni ? ua : pa[k]; }
-  __device__ __forceinline__ float s(int k) const { return uni ? us : ps[k]; }
+  __device__ __forceinline__ float a(int k) const { return pa[k]; }
+  __device__ __forceinline__ float s(int k) const { return ps[k]; }
 };
 // One value for every entry (per-tensor / group amax modes).
 struct UniformTab {
@@ -484,6 +507,9 @@ struct ITSmem {
   float ra[4][32], rs[4][32];
   // column amax / S_enc of the strip's 256 columns
   float ca[IT_COLS], cs[IT_COLS];
+  // row-group mode: the group amax / S_enc of each wave half's 16-row block,
+  // repeated for the lane's 8 columns
+  float ga[4][2][8], gs[4][2][8];
 };
 
 struct StoreIT {
@@ -555,8 +581,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     return make_rsrc(x + (rs + 32 * wv) * K + c0, (int64_t)32 * K * (int64_t)sizeof(T));
   };
   // The first PF rows of each half of the wave's next sub-step are loaded while
-  // the current one's columnwise half runs (BF16: 32 registers; FP32 has none
-  // to spare).
+  // the current one's block scales and codes are computed (BF16: 32 registers;
+  // FP32 has none to spare). Loading all 16 rows ahead needs 32 more registers
+  // than a wave has at 2 waves per SIMD and ends up slower.
   constexpr int PF = sizeof(T) == 2 ? 8 : 0;
   uint32_t pf[PF > 0 ? PF : 1][NW];
   auto prefetch = [&](int64_t rs, int64_t c0) {
@@ -577,12 +604,16 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     // column amax / S_enc: the strip's table in LDS (modes 0 and 1, filled
     // when the strip changes), or the group amax of the lane's 16-row block
     // (mode 2)
-    ColSel ctab{&sm.ca[8 * L], &sm.cs[8 * L], 0.0f, 1.0f, false};
+    ColLds ctab{&sm.ca[8 * L], &sm.cs[8 * L]};
     if constexpr (COLW) {
       if (p.col_mode == 2) {
-        ctab.uni = true;
-        ctab.ua = p.col_amax[rs + 32 * wv + 16 * h];
-        ctab.us = global_encode_scale(ctab.ua, p.F);
+        if (L < 8) {
+          const float a = p.col_amax[rs + 32 * wv + 16 * h];
+          sm.ga[wv][h][L] = a;
+          sm.gs[wv][h][L] = global_encode_scale(a, p.F);
+        }
+        __builtin_amdgcn_wave_barrier();
+        ctab = ColLds{&sm.ga[wv][h][0], &sm.gs[wv][h][0]};
       } else if (c0 != c0_tab) {
         const float a = p.col_amax[p.col_mode == 0 ? 0 : c0 + tid];
         __syncthreads();  // every wave is done with the previous strip's table

@@ -98,6 +98,27 @@ __device__ __forceinline__ void block_scale(float bamax, float a, float s_enc, f
   *enc = (d == 0.0f) ? 0.0f : recip_rn(d);
 }
 
+// block_scale without its range guards, for the batched block code: the same
+// results whenever bamax >= 2^-125 (div6_rn's fast form) and D lies in
+// [2^-126, 2^126) (recip_rn's fast form; then D != 0 too), which it reports.
+// *byte is the converter's packed result: its low byte is the scale byte.
+// Callers redo the lanes where it returns false with block_scale.
+__device__ __forceinline__ bool block_scale_fast(float bamax, float a, float s_enc, float f_inv,
+                                                 uint32_t* byte, float* enc) {
+  constexpr float kR6 = 0.16666667163372039794921875f;  // RN(1/6)
+  const float q0 = bamax * kR6;
+  const float q = __builtin_fmaf(__builtin_fmaf(-q0, kE2M1Max, bamax), kR6, q0);
+  const float s32 = fminf(q * s_enc, kE4M3Max);
+  const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(s32, s32, 0, false);
+  *byte = (uint32_t)pk;
+  const float sq = __builtin_amdgcn_cvt_f32_fp8(pk, 0);
+  const float d = (sq * a) * f_inv;
+  const float r = __builtin_amdgcn_rcpf(d);
+  *enc = __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+  const uint32_t bb = __float_as_uint(bamax), db = __float_as_uint(d);
+  return (bb >= 0x01000000u) & ((db - 0x00800000u) < 0x7E000000u);
+}
+
 // --------------------------------------------------------------- E2M1 encode
 // v_cvt_scalef32_pk_fp4_f32 with scale 1.0 converts two fp32 values to E2M1
 // with round-to-nearest-even, saturation at 6 and the sign bit kept (-0 and
