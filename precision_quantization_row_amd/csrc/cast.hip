@@ -398,10 +398,10 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
     }
   }
 
-  // ---- phase 3: codes
+  // ---- phase 3: codes. Byte j & 3 of cc[k][j >> 2] holds rows 2j, 2j+1 of
+  // column k; byte 0 starts from the first product's own bits (the other bytes
+  // are written later), so the accumulators need no zeroing.
   uint32_t cc[8][2];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) cc[k][0] = cc[k][1] = 0u;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float xv[2][8];
@@ -419,8 +419,10 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
     }
     if constexpr (COLW) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        cc[k][j >> 2] = cvt_fp4x2_sel(cc[k][j >> 2], xv[0][k] * cenc[k], xv[1][k] * cenc[k], j);
+      for (int k = 0; k < 8; ++k) {
+        const float p0 = xv[0][k] * cenc[k], p1 = xv[1][k] * cenc[k];
+        cc[k][j >> 2] = cvt_fp4x2_sel((j & 3) ? cc[k][j >> 2] : __float_as_uint(p0), p0, p1, j);
+      }
     }
   }
   if constexpr (COLW) {
@@ -565,12 +567,14 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
 
   // sub-step v: macro tile origin (m0, c0); false when outside the interior
   // (uniform per workgroup, the same for both sub-steps of a tile)
+  // (32-bit index arithmetic: the host sends only grids whose tile counts fit)
   auto tile_of = [&](int64_t v, int64_t& m0, int64_t& c0) -> bool {
-    const int64_t t = (v >> 1) * per + jw;
-    const int64_t strip = xcd * spx + t / nmr;
-    m0 = (t % nmr) * IT_MACRO;
+    const uint32_t t = (uint32_t)(v >> 1) * (uint32_t)per + (uint32_t)jw;
+    const uint32_t q = t / (uint32_t)nmr, r = t - q * (uint32_t)nmr;
+    const int64_t strip = xcd * spx + q;
+    m0 = (int64_t)r * IT_MACRO;
     c0 = strip * IT_COLS;
-    return t < ntiles_x && strip < nstrips;
+    return t < (uint64_t)ntiles_x && strip < nstrips;
   };
   auto next_sub = [&](int64_t v, int64_t& m0, int64_t& c0) -> int64_t {
     while (v < n_v && !tile_of(v, m0, c0)) ++v;
@@ -890,6 +894,10 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
                     (int64_t)32 * a.K * (int64_t)sizeof(T) < lim;
   k.n_istrips = fast ? a.K / IT_COLS : 0;
   k.n_isteps = fast ? a.M / IT_MACRO : 0;
+  // the kernel indexes macro tiles with 32-bit arithmetic: tiles per XCD and
+  // sub-steps per workgroup stay far below 2^31
+  if (k.n_isteps * ((k.n_istrips + IT_XCDS - 1) / IT_XCDS) >= ((int64_t)1 << 30))
+    k.n_istrips = k.n_isteps = 0;
   if (k.n_istrips == 0 || k.n_isteps == 0) k.n_istrips = k.n_isteps = 0;
   const bool rw = a.q_row != nullptr, cw = a.q_col != nullptr;
   if (rw && cw) launch_cast_kernels<T, true, true>(k, a, s);

@@ -129,11 +129,12 @@ __device__ __forceinline__ bool block_scale_fast(float bamax, float a, float s_e
 #define NVFP4_CVT_FP4X2(old, v0, v1, SEL) \
   __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (v0), (v1), 1.0f, (SEL))
 
-// Eight elements -> one dword of eight nibbles (element k in nibble k).
+// Eight elements -> one dword of eight nibbles (element k in nibble k). All
+// four bytes are written, so the first convert may start from any value: it
+// takes v0's own bits, a register that dies there (no zeroing move).
 __device__ __forceinline__ uint32_t e2m1_pack8(float v0, float v1, float v2, float v3, float v4,
                                                float v5, float v6, float v7) {
-  uint32_t w = 0u;
-  w = NVFP4_CVT_FP4X2(w, v0, v1, 0);
+  uint32_t w = NVFP4_CVT_FP4X2(__float_as_uint(v0), v0, v1, 0);
   w = NVFP4_CVT_FP4X2(w, v2, v3, 1);
   w = NVFP4_CVT_FP4X2(w, v4, v5, 2);
   w = NVFP4_CVT_FP4X2(w, v6, v7, 3);
