@@ -38,8 +38,9 @@ __global__ void __launch_bounds__(256) amax_init_kernel(float* ra, int64_t M, fl
 // ------------------------------------------------------------- fused (BF16)
 // Workgroup = 4 waves; a wave's 16-lane DPP row g reads 16 x 16 B = 128
 // consecutive BF16 of one row per load, so every load instruction fetches 4
-// full 256-byte row segments. The tile is FUSED_TR rows x (128 * FUSED_NC)
-// columns; the 16 (wave, row-group) slots take rows slot, slot + 16, ...
+// full 256-byte row segments. The tile is tr rows x (128 * FUSED_NC) columns
+// (tr = 256, or fewer for small matrices so that the grid still fills the
+// GPU); the 16 (wave, row-group) slots take rows slot, slot + 16, ...
 // Each lane keeps the running column max of its 8 * FUSED_NC columns in
 // registers as packed u16 magnitudes (v_pk_max_u16), so the column reduction
 // is a register reduction over rows -- no strided global read and no LDS
@@ -47,14 +48,14 @@ __global__ void __launch_bounds__(256) amax_init_kernel(float* ra, int64_t M, fl
 // and published per row; column maxima of the 16 slots meet once in LDS at the
 // end of the tile and are published per column.
 constexpr int FUSED_NC = 4;    // 128-column chunks per tile -> 512 columns
-constexpr int FUSED_TR = 256;  // rows per tile
+constexpr int FUSED_TR = 256;  // rows per tile (largest)
 
 __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __restrict__ x,
                                                               int64_t M, int64_t K,
                                                               float* __restrict__ ra,
                                                               float* __restrict__ ca,
                                                               const float* noop,
-                                                              int64_t tiles_c) {
+                                                              int64_t tiles_c, int64_t tr) {
   if (skip(noop)) return;
   __shared__ uint32_t colmax_s[16][FUSED_NC * 64 + 1];
   const int tid = threadIdx.x;
@@ -62,7 +63,7 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
   const int q = lane & 15;           // lane within the DPP row
   const int slot = (tid >> 6) * 4 + (lane >> 4);  // 0..15
   const int64_t tile = blockIdx.x;
-  const int64_t r0 = (tile / tiles_c) * FUSED_TR;
+  const int64_t r0 = (tile / tiles_c) * tr;
   const int64_t c0 = (tile % tiles_c) * (128 * FUSED_NC);
 
   uint32_t cm[FUSED_NC][4];
@@ -75,7 +76,7 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
 #pragma unroll
   for (int j = 0; j < FUSED_NC; ++j) colok[j] = (c0 + 128 * j) < K;  // K % 128 == 0
 
-  const int64_t rend = min(r0 + (int64_t)FUSED_TR, M);
+  const int64_t rend = min(r0 + tr, M);
 #pragma unroll 2
   for (int64_t r = r0 + slot; r < rend; r += 16) {
     const uint4* rowp = reinterpret_cast<const uint4*>(x + r * K + c0) + q;
@@ -301,9 +302,14 @@ int launch_amax_init(float* ra, int64_t M, float* ca, int64_t K, float* ta, cons
 int launch_fused_amax_bf16(const void* x, int64_t M, int64_t K, float* ra, float* ca,
                            const float* noop, hipStream_t s) {
   const int64_t tiles_c = (K + 128 * FUSED_NC - 1) / (128 * FUSED_NC);
-  const int64_t tiles_r = (M + FUSED_TR - 1) / FUSED_TR;
+  // Tall tiles publish fewer column maxima; short ones give more workgroups.
+  // Take the tallest tile (256 .. 32 rows) that still gives about 6
+  // workgroups per CU.
+  int64_t tr = FUSED_TR;
+  while (tr > 32 && ((M + tr - 1) / tr) * tiles_c < (int64_t)num_cus() * 6) tr /= 2;
+  const int64_t tiles_r = (M + tr - 1) / tr;
   hipLaunchKernelGGL(fused_amax_bf16_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), M, K, ra, ca, noop, tiles_c);
+                     static_cast<const uint16_t*>(x), M, K, ra, ca, noop, tiles_c, tr);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
