@@ -830,7 +830,8 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
     const int64_t G = interior_grid<T, ROWW, COLW>();
     hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW>), dim3((unsigned)G), dim3(256), 0, s,
                        k);
-  }  // edge rectangles: (1) the partial last strip over all rows,
+  }
+  // edge rectangles: (1) the partial last strip over all rows,
   // (2) the rows below the interior for the full strips
   auto edge = [&](int64_t rstart, int64_t rend, int64_t strip0, int64_t nstrips) {
     if (rend <= rstart || nstrips <= 0) return;
