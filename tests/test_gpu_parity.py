@@ -53,6 +53,24 @@ def test_small_forced_two_kernel(shape):
     check_row_scaled(w.x, flags=p.NVFP4_FLAG_FORCE_TWO_KERNEL, dequant=False, label="two-kernel")
 
 
+@pytest.mark.parametrize("M,K", [(128, 128), (384, 640), (1152, 2304), (4224, 1024), (8192, 128),
+                                 (4224, 24576)])
+def test_fused_amax_tile_heights(M, K):
+    """The fused amax picks its tile height per shape, 256 rows down to 32:
+    32-row tiles for the small shapes here (with a partial last column tile
+    when K is not a multiple of 512), 128-row tiles for 4224 x 24576. The
+    full-size workload tests cover 256 (8192 x 28672) and 64 (grouped
+    tokens). Every choice gives the exact maxima."""
+    say(f"[gpu] fused amax tile heights {M}x{K}")
+    g = torch.Generator().manual_seed(M + K)
+    x = (torch.randn(M, K, generator=g) * torch.exp(torch.randn(M, 1, generator=g) * 3)).to(torch.bfloat16)
+    assert p.nvfp4_amax_path(p.NVFP4_BF16, M, K, 1, 1, 0) == 1
+    ra, ca, _ = gpu_amax(x.to(DEV))
+    xf = x.float().numpy()
+    assert_same("row_amax", f32_bits(ra), oracle.amax_rows(xf).view(np.uint32))
+    assert_same("col_amax", f32_bits(ca), oracle.amax_cols(xf).view(np.uint32))
+
+
 def test_fused_equals_two_kernel_bytes():
     """Fused-amax PR description: the fused pass is an exact max, so its
     results are byte-identical to the two-kernel path."""
