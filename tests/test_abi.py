@@ -85,6 +85,10 @@ def test_validation_rejects_before_launch():
     assert q(448.0, ra=None) == E
     assert q(448.0, rm=2) == E      # ROWGROUP is for the transposed copy only
     assert q(448.0, cm=3) == E
+    # empty matrices are rejected, not launched
+    for M, K in ((0, 32), (32, 0), (-1, 32)):
+        assert lib.nvfp4_quantize_transpose(_fake(), 0, M, K, 1, _fake(), 1, _fake(), f(448.0),
+                                            _fake(), _fake(), _fake(), _fake(), None, None) == E
     # dequantize
     d = lambda mode=1, out=0, bound=448.0, R=4, C=16: lib.nvfp4_dequantize(
         _fake(), _fake(), R, C, mode, _fake(), f(bound), _fake(), out, None, None)
@@ -92,6 +96,7 @@ def test_validation_rejects_before_launch():
     assert d(out=2) == E
     assert d(bound=500.0) == E
     assert d(R=0) == E
+    assert d(C=0) == E
     # group expansion
     assert lib.nvfp4_group_amax_expand(_fake(), 16, _fake(), 0, None, None) == E
     assert lib.nvfp4_group_amax_expand(None, 16, _fake(), 2, None, None) == E
