@@ -60,12 +60,81 @@ def measured_traffic():
     return rec.get("cast_hbm_bytes_per_launch")
 
 
+def _row(us, nbytes, what):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 2), "bytes": nbytes, "GBs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_are": what}
+
+
+def other_rows(p, workloads, torch, dev, xs, timed, bound):
+    """The remaining kernels of the path, each on the workload it serves,
+    timed alone (back-to-back launches, events at the region's ends). Bytes
+    are those each launch actually has to move (the two-kernel amax reads X
+    twice)."""
+    n = 20
+    res = {}
+    x = xs[0]
+    M, K = x.shape
+    ra = torch.empty(M, dtype=torch.float32, device=dev)
+    ca = torch.empty(K, dtype=torch.float32, device=dev)
+    ta = torch.empty(1, dtype=torch.float32, device=dev)
+    xb = M * K * 2
+    f2 = lambda i: p.nvfp4_amax_rowcol(xs[i & 1], ra, ca, flags=p.NVFP4_FLAG_FORCE_TWO_KERNEL)
+    f2(0)
+    res["two_kernel_amax_bf16_8192x28672"] = _row(timed(f2, n) * 1e3, 2 * xb + 4 * (M + K),
+                                                  "X read by each of the two kernels, vectors written")
+    ft = lambda i: p.nvfp4_amax_rowcol(xs[i & 1], None, None, tensor_amax=ta)
+    ft(0)
+    res["tensor_amax_bf16_8192x28672"] = _row(timed(ft, n) * 1e3, xb + 4, "X read once")
+
+    w = workloads.make("fp32_edge")
+    M, K = w.shape
+    x = w.x.to(dev)
+    ra = torch.empty(M, dtype=torch.float32, device=dev)
+    ca = torch.empty(K, dtype=torch.float32, device=dev)
+    out = p.empty_outputs(M, K, dev)
+    fa = lambda i: p.nvfp4_amax_rowcol(x, ra, ca)
+    fc = lambda i: p.nvfp4_quantize_transpose(x, 1, ra, 1, ca, bound, out["q_row"], out["s_row"],
+                                              out["q_col"], out["s_col"])
+    fa(0); fc(0)
+    cb = M * K * 4 + 4 * (M + K) + M * ((K + 1) // 2) + M * ((K + 15) // 16) + K * ((M + 1) // 2) \
+        + K * ((M + 15) // 16)
+    res["fp32_4097x2880_two_kernel_amax"] = _row(timed(fa, n) * 1e3, 2 * M * K * 4 + 4 * (M + K),
+                                                 "X read by each of the two kernels")
+    res["fp32_4097x2880_cast"] = _row(timed(fc, n) * 1e3, cb, "X read once, both copies written")
+    del x, out
+
+    w = workloads.make("moe_groups")
+    M, K = w.shape
+    x = w.x.to(dev)
+    ge = w.group_end.to(dev)
+    ra = torch.empty(M, dtype=torch.float32, device=dev)
+    out = p.empty_outputs(M, K, dev)
+    def moe(i):
+        # per-group amax: row amax expanded over each group, colwise blocks use
+        # the group amax of their rows
+        p.nvfp4_amax_rowcol(x, ra)
+        p.nvfp4_group_amax_expand(ra, ge)
+        p.nvfp4_quantize_transpose(x, 1, ra, 2, ra, bound, out["q_row"], out["s_row"],
+                                   out["q_col"], out["s_col"])
+    moe(0)
+    mb = 2 * M * K * 2 + 4 * 4 * M + 8 * ge.numel() + M * ((K + 1) // 2) + M * ((K + 15) // 16) \
+        + K * ((M + 1) // 2) + K * ((M + 15) // 16)
+    res["moe_%dx%d_amax_expand_cast" % (M, K)] = _row(timed(moe, n) * 1e3, mb,
+                                                       "X read by the amax and the cast passes")
+    del x, out
+    return res
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the other kernels of the path (two-kernel amax, per-tensor "
+                         "amax, FP32 and grouped-token workloads)")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -159,19 +228,14 @@ def main():
 
     # dequantize the rowwise copy to BF16 (reported beside the step, not in it)
     y = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        p.nvfp4_dequantize(out["q_row"], out["s_row"], M, K, 1, ra, bound, y)
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    nd = 10
-    d0.record()
-    for _ in range(nd):
-        p.nvfp4_dequantize(out["q_row"], out["s_row"], M, K, 1, ra, bound, y)
-    d1.record()
-    torch.cuda.synchronize()
-    dq_ms = d0.elapsed_time(d1) / nd
+    dq = lambda i: p.nvfp4_dequantize(out["q_row"], out["s_row"], M, K, 1, ra, bound, y)
+    for i in range(3):
+        dq(i)
+    dq_ms = timed(dq, 10)
     dq_bytes = M * ((K + 1) // 2) + M * ((K + 15) // 16) + 4 * M + M * K * 2
     del y
+
+    row_meas = {} if args.no_rows else other_rows(p, workloads, torch, dev, xs, timed, bound)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -222,7 +286,9 @@ def main():
                        "amax_GBs": round(amax_bytes / (amax_avg * 1e-3) / 1e9, 1),
                        "how": "each kind launched alone, back to back, same inputs"},
         "dequant_rowwise_bf16": {"us": round(dq_ms * 1e3, 2),
-                                 "GBs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1)},
+                                 "GBs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1),
+                                 "frac": round(dq_bytes / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "other_rows": row_meas,
         "cpu_baseline": cpu,
         "source_digest": source_digest(),
     }
