@@ -51,8 +51,9 @@ struct CastK {
   int row_store4;  // K % 8 == 0: rowwise code rows are dword aligned
   int col_store8;  // M % 16 == 0: transposed code rows are 8-byte aligned
   // interior kernel: macro tiles of 256 rows x 256 columns, n_istrips strips
-  // by n_isteps macro rows
-  int64_t n_istrips, n_isteps;
+  // by n_isteps macro rows; if half_last, the last macro row is 128 rows (its
+  // first sub-step only)
+  int64_t n_istrips, n_isteps, half_last;
   // edge kernel: rows [rstart, rend) in segments of rows_per_wg (a multiple of
   // CAST_STEP_ROWS, <= CAST_MAX_ROWS_PER_WG); workgroup b takes segment
   // seg0 + b / nstrips of strip strip0 + b % nstrips
@@ -574,7 +575,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     const int64_t strip = xcd * spx + q;
     m0 = (int64_t)r * IT_MACRO;
     c0 = strip * IT_COLS;
-    return t < (uint64_t)ntiles_x && strip < nstrips;
+    const bool cut = p.half_last && r == (uint32_t)nmr - 1 && (v & 1);  // half macro tile
+    return t < (uint64_t)ntiles_x && strip < nstrips && !cut;
   };
   auto next_sub = [&](int64_t v, int64_t& m0, int64_t& c0) -> int64_t {
     while (v < n_v && !tile_of(v, m0, c0)) ++v;
@@ -679,13 +681,18 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
             *reinterpret_cast<const uint4*>(&sm.sr[sbuf][tid][0]);
     }
     sbuf ^= 1;
-    if (COLW && sub == 1) {
+    // a half macro tile (the last macro row of a matrix with M % 256 = 128)
+    // is flushed after its only sub-step: 64 B of codes and 8 scale bytes per
+    // column
+    const bool half = p.half_last && m0 == (nmr - 1) * IT_MACRO;
+    if (COLW && (sub == 1 || half)) {
       // 256 columns x 128 B of transposed codes: 8 lanes per column, whole
       // lines, slots restored to row order
 #pragma unroll
       for (int it = 0; it < IT_COLS * 8 / 256; ++it) {
         const int pidx = tid + 256 * it;
         const int c = pidx >> 3, t = pidx & 7;
+        if (half && t >= 4) continue;
         const int f = (c >> 3) & 15;
         u32x4 q = *reinterpret_cast<const u32x4*>(&sm.qc[mbuf][c ^ (f & 1)][16 * (t ^ (f >> 1))]);
         if (f & 1) q = (u32x4){q.z, q.w, q.x, q.y};
@@ -697,11 +704,12 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
         const u32x4 q = *reinterpret_cast<const u32x4*>(&sm.sc[mbuf][tid][0]);
         const int c = 8 * (tid & 31) + (tid >> 5);
         uint8_t* dst = p.s_col + (c0 + c) * scs + m0 / 16;
-        if ((scs & 15) == 0) {
+        if ((scs & 15) == 0 && !half) {
           *reinterpret_cast<u32x4*>(dst) = q;
         } else {
           uint32_t* d4 = reinterpret_cast<uint32_t*>(dst);
-          d4[0] = q.x; d4[1] = q.y; d4[2] = q.z; d4[3] = q.w;
+          d4[0] = q.x; d4[1] = q.y;
+          if (!half) { d4[2] = q.z; d4[3] = q.w; }
         }
       }
       mbuf ^= 1;
@@ -854,7 +862,7 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
   };
   const int64_t strips = (a.K + CAST_STRIP_COLS - 1) / CAST_STRIP_COLS;
   if (ntiles > 0)  // the interior spans every column: the rows below it remain
-    edge(k.n_isteps * IT_MACRO, a.M, 0, strips);
+    edge(k.n_isteps * IT_MACRO - (k.half_last ? IT_SUB : 0), a.M, 0, strips);
   else
     edge(0, a.M, 0, strips);
 }
@@ -896,11 +904,13 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
                     (int64_t)32 * a.K * (int64_t)sizeof(T) < lim;
   k.n_istrips = fast ? a.K / IT_COLS : 0;
   k.n_isteps = fast ? a.M / IT_MACRO : 0;
+  k.half_last = fast && (a.M % IT_MACRO) >= IT_SUB;  // one more, 128-row macro row
+  k.n_isteps += k.half_last;
   // the kernel indexes macro tiles with 32-bit arithmetic: tiles per XCD and
   // sub-steps per workgroup stay far below 2^31
   if (k.n_isteps * ((k.n_istrips + IT_XCDS - 1) / IT_XCDS) >= ((int64_t)1 << 30))
     k.n_istrips = k.n_isteps = 0;
-  if (k.n_istrips == 0 || k.n_isteps == 0) k.n_istrips = k.n_isteps = 0;
+  if (k.n_istrips == 0 || k.n_isteps == 0) k.n_istrips = k.n_isteps = k.half_last = 0;
   const bool rw = a.q_row != nullptr, cw = a.q_col != nullptr;
   if (rw && cw) launch_cast_kernels<T, true, true>(k, a, s);
   else if (rw) launch_cast_kernels<T, true, false>(k, a, s);

@@ -71,6 +71,16 @@ def test_fused_amax_tile_heights(M, K):
     assert_same("col_amax", f32_bits(ca), oracle.amax_cols(xf).view(np.uint32))
 
 
+@pytest.mark.parametrize("M,K", [(128, 256), (384, 768), (640, 256), (192, 512), (448, 512)])
+def test_interior_half_macro_tiles(M, K):
+    """M % 256 = 128 or 192: the interior kernel's last macro row is a 128-row
+    half tile (flushed after one sub-step), and for 192 the last 64 rows go to
+    the edge kernel."""
+    g = torch.Generator().manual_seed(3 * M + K)
+    x = (torch.randn(M, K, generator=g) * torch.pow(10.0, torch.rand(M, 1, generator=g) * 4 - 2))
+    check_row_scaled(x.to(torch.bfloat16), bounds=(448.0,), label=f"half tiles {M}x{K}")
+
+
 def test_fused_equals_two_kernel_bytes():
     """Fused-amax PR description: the fused pass is an exact max, so its
     results are byte-identical to the two-kernel path."""
