@@ -44,9 +44,9 @@ __global__ void __launch_bounds__(256) amax_init_kernel(float* ra, int64_t M, fl
 // Each lane keeps the running column max of its 8 * FUSED_NC columns in
 // registers as packed u16 magnitudes (v_pk_max_u16), so the column reduction
 // is a register reduction over rows -- no strided global read and no LDS
-// staging of the tile. Row maxima are reduced across the 16 lanes with DPP
-// and published per row; column maxima of the 16 slots meet once in LDS at the
-// end of the tile and are published per column.
+// staging of the tile. Row maxima are reduced across the 16 lanes with DPP;
+// column maxima of the 16 slots meet once in LDS; both are published with
+// atomic max at the end of the tile, one per row and one per column.
 constexpr int FUSED_NC = 4;    // 128-column chunks per tile -> 512 columns
 constexpr int FUSED_TR = 256;  // rows per tile (largest)
 
@@ -58,6 +58,7 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
                                                               int64_t tiles_c, int64_t tr) {
   if (skip(noop)) return;
   __shared__ uint32_t colmax_s[16][FUSED_NC * 64 + 1];
+  __shared__ uint32_t rowmax_s[FUSED_TR];  // the tile's row maxima, published at the end
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int q = lane & 15;           // lane within the DPP row
@@ -97,7 +98,7 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
     }
     uint32_t rbits = max(rm & 0xFFFFu, rm >> 16) << 16;
     rbits = row16_max(rbits);
-    if (q == 0) atomicMax(reinterpret_cast<unsigned int*>(ra + r), rbits);
+    if (q == 0) rowmax_s[r - r0] = rbits;  // row r has one writer in the tile
   }
 
   // column maxima: the 16 slots meet in LDS, one atomic per column per tile
@@ -106,6 +107,10 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
 #pragma unroll
     for (int d = 0; d < 4; ++d) colmax_s[slot][j * 64 + q * 4 + d] = cm[j][d];
   __syncthreads();
+  // Row maxima are published here rather than inside the load loop: a
+  // memory atomic there sits in the same in-order counter as the loads and
+  // holds up the waits for the next rows.
+  if (tid < rend - r0) atomicMax(reinterpret_cast<unsigned int*>(ra + r0 + tid), rowmax_s[tid]);
   // 256 threads, FUSED_NC * 64 dwords = 2 * FUSED_NC * 64 columns
   for (int e = tid; e < FUSED_NC * 64; e += 256) {
     uint32_t m = 0u;
