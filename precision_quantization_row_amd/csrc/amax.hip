@@ -49,6 +49,7 @@ __global__ void __launch_bounds__(256) amax_init_kernel(float* ra, int64_t M, fl
 // atomic max at the end of the tile, one per row and one per column.
 constexpr int FUSED_NC = 4;    // 128-column chunks per tile -> 512 columns
 constexpr int FUSED_TR = 256;  // rows per tile (largest)
+constexpr int FUSED_RU = 2;    // rows per slot per loop iteration
 
 __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __restrict__ x,
                                                               int64_t M, int64_t K,
@@ -78,27 +79,37 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
   for (int j = 0; j < FUSED_NC; ++j) colok[j] = (c0 + 128 * j) < K;  // K % 128 == 0
 
   const int64_t rend = min(r0 + tr, M);
-#pragma unroll 2
-  for (int64_t r = r0 + slot; r < rend; r += 16) {
-    const uint4* rowp = reinterpret_cast<const uint4*>(x + r * K + c0) + q;
-    uint4 v[FUSED_NC];
+  // FUSED_RU rows per slot and iteration, all loads issued before any use
+  // (rows past rend are skipped; with M % 128 == 0 and tr a multiple of 32
+  // that only happens for RU = 4 and 32-row tiles)
+  for (int64_t rb = r0 + slot; rb < rend; rb += 16 * FUSED_RU) {
+    uint4 v[FUSED_RU][FUSED_NC];
 #pragma unroll
-    for (int j = 0; j < FUSED_NC; ++j)
-      v[j] = colok[j] ? rowp[16 * j] : make_uint4(0, 0, 0, 0);
-    uint32_t rm = 0u;
+    for (int u = 0; u < FUSED_RU; ++u) {
+      const int64_t r = rb + 16 * u;
+      const uint4* rowp = reinterpret_cast<const uint4*>(x + r * K + c0) + q;
 #pragma unroll
-    for (int j = 0; j < FUSED_NC; ++j) {
-      const uint32_t a0 = v[j].x & kAbsBf16x2, a1 = v[j].y & kAbsBf16x2;
-      const uint32_t a2 = v[j].z & kAbsBf16x2, a3 = v[j].w & kAbsBf16x2;
-      cm[j][0] = pk_max_u16(cm[j][0], a0);
-      cm[j][1] = pk_max_u16(cm[j][1], a1);
-      cm[j][2] = pk_max_u16(cm[j][2], a2);
-      cm[j][3] = pk_max_u16(cm[j][3], a3);
-      rm = pk_max_u16(rm, pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3)));
+      for (int j = 0; j < FUSED_NC; ++j)
+        v[u][j] = (colok[j] && r < rend) ? rowp[16 * j] : make_uint4(0, 0, 0, 0);
     }
-    uint32_t rbits = max(rm & 0xFFFFu, rm >> 16) << 16;
-    rbits = row16_max(rbits);
-    if (q == 0) rowmax_s[r - r0] = rbits;  // row r has one writer in the tile
+#pragma unroll
+    for (int u = 0; u < FUSED_RU; ++u) {
+      const int64_t r = rb + 16 * u;
+      uint32_t rm = 0u;
+#pragma unroll
+      for (int j = 0; j < FUSED_NC; ++j) {
+        const uint32_t a0 = v[u][j].x & kAbsBf16x2, a1 = v[u][j].y & kAbsBf16x2;
+        const uint32_t a2 = v[u][j].z & kAbsBf16x2, a3 = v[u][j].w & kAbsBf16x2;
+        cm[j][0] = pk_max_u16(cm[j][0], a0);
+        cm[j][1] = pk_max_u16(cm[j][1], a1);
+        cm[j][2] = pk_max_u16(cm[j][2], a2);
+        cm[j][3] = pk_max_u16(cm[j][3], a3);
+        rm = pk_max_u16(rm, pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3)));
+      }
+      uint32_t rbits = max(rm & 0xFFFFu, rm >> 16) << 16;
+      rbits = row16_max(rbits);
+      if (q == 0 && r < rend) rowmax_s[r - r0] = rbits;  // row r has one writer in the tile
+    }
   }
 
   // column maxima: the 16 slots meet in LDS, one atomic per column per tile
