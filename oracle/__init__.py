@@ -223,3 +223,50 @@ def to_bf16_bits(y: np.ndarray) -> np.ndarray:
 
     t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(torch.bfloat16)
     return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------ grouped tokens
+def pad_groups(x_tokens, group_rows, align: int, m_out: int) -> np.ndarray:
+    """Grouped-GEMM PR description (ragged token groups zero-padded to 128-row
+    alignment before quantization): the G groups of x_tokens [T][K] (group g
+    holds group_rows[g] consecutive rows) laid out in an [m_out][K] matrix,
+    group g starting at the sum of the earlier groups' sizes rounded up to
+    `align`, every other row zero. Rows that do not fit in m_out are
+    dropped; token rows past T read as zero."""
+    x = _f32(x_tokens)
+    T, K = x.shape
+    out = np.zeros((m_out, K), dtype=np.float32)
+    p = t = 0
+    for n in np.asarray(group_rows, dtype=np.int64).tolist():
+        for r in range(n):
+            if p + r < m_out and t + r < T:
+                out[p + r] = x[t + r]
+        t += n
+        p += -(-n // align) * align
+    return out
+
+
+def padded_group_end(group_rows, align: int, m_out: int) -> np.ndarray:
+    """End row (exclusive) of every padded group, clipped to m_out."""
+    ends, p = [], 0
+    for n in np.asarray(group_rows, dtype=np.int64).tolist():
+        p += -(-n // align) * align
+        ends.append(min(p, m_out))
+    return np.asarray(ends, dtype=np.int64)
+
+
+def quantize_grouped(x_tokens, group_rows, align: int, m_out: int, bound: float = 448.0):
+    """Grouped tokens, padded on the way in: per-group amax expanded over each
+    padded group (rows past the last group get 0), rowwise codes with that
+    per-row amax, transposed codes with the group amax of each 16-row block
+    (grouped-GEMM PR description: equal to quantizing each split on its own).
+    Returns (row_amax [m_out], q_row, s_row, q_col, s_col)."""
+    xp = pad_groups(x_tokens, group_rows, align, m_out)
+    ends = padded_group_end(group_rows, align, m_out)
+    last = int(ends[-1]) if ends.size else 0
+    ra = np.zeros(m_out, dtype=np.float32)
+    if last:
+        ra[:last] = group_amax_expand(amax_rows(xp[:last]), ends)
+    q_row, s_row = quantize_rowwise(xp, MODE_LINE, ra, bound)
+    q_col, s_col = quantize_colwise(xp, MODE_ROWGROUP, ra, bound)
+    return ra, q_row, s_row, q_col, s_col
