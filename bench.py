@@ -122,7 +122,22 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
         + K * ((M + 1) // 2) + K * ((M + 15) // 16)
     res["moe_%dx%d_amax_expand_cast" % (M, K)] = _row(timed(moe, n) * 1e3, mb,
                                                        "X read by the amax and the cast passes")
-    del x, out
+    del x
+
+    # the same groups as token rows, padded on the way in by one call
+    starts = torch.cat([torch.zeros(1, dtype=torch.int64), w.group_end[:-1]])
+    tok = torch.cat([w.x[int(s):int(s) + int(r)] for s, r in zip(starts, w.group_rows)]).to(dev)
+    T = tok.shape[0]
+    gr = w.group_rows.to(dev)
+    def grouped(i):
+        p.nvfp4_quantize_grouped(tok, gr, 128, M, bound, ra, out["q_row"], out["s_row"],
+                                 out["q_col"], out["s_col"])
+    grouped(0)
+    gb = 2 * T * K * 2 + 4 * M + 8 * gr.numel() + M * ((K + 1) // 2) + M * ((K + 15) // 16) \
+        + K * ((M + 1) // 2) + K * ((M + 15) // 16)
+    res["moe_%dtok_x%d_quantize_grouped" % (T, K)] = _row(
+        timed(grouped, n) * 1e3, gb, "token rows read by the amax and the cast, padded layout written")
+    del tok, out
     return res
 
 

@@ -130,6 +130,38 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
                              float bound, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
                              uint8_t* s_col, const float* noop, void* stream);
 
+/* Grouped tokens, padded on the way in, in one call (grouped-GEMM PR
+ * description: ragged token groups zero-padded to an alignment before
+ * quantization, per-group global scales from each group's amax expanded to
+ * its rows, so that the call equals quantizing each group on its own;
+ * padded rows quantize to zero codes). The group sizes stay on the device
+ * and no pointer lists are involved, so the call has a fixed shape for a
+ * captured graph.
+ *   x          [T][K] BF16 or FP32: the G groups back to back (group g holds
+ *              group_rows[g] rows); token rows past the groups are ignored,
+ *              and group rows past T read as zero rows
+ *   group_rows [G] device int64, entries >= 0 (negative entries count as
+ *              0); 1 <= G <= NVFP4_GROUPS_MAX
+ *   align      a multiple of 16 in [16, 4096] (128 in the pages' recipe)
+ *   M_out      rows of the padded layout the outputs hold. Group g occupies
+ *              rows [P_g, P_{g+1}), P_0 = 0, P_{g+1} = P_g + group_rows[g]
+ *              rounded up to align; rows past P_G are zero rows. Rows that
+ *              do not fit in M_out are dropped (and take no part in their
+ *              group's amax), so size M_out for the worst case
+ *              (T + G * (align - 1), rounded up to align).
+ *   row_amax   [M_out] float, written: the group amax on every row of a
+ *              group, 0 past P_G
+ *   q_row [M_out][ceil(K/2)], s_row [M_out][ceil(K/16)] (both or neither)
+ *   q_col [K][ceil(M_out/2)], s_col [K][ceil(M_out/16)] (both or neither):
+ *              rowwise codes with the per-row amax, transposed codes with
+ *              the group amax of each 16-row block (as mode ROWGROUP)
+ * At least one copy must be requested. */
+#define NVFP4_GROUPS_MAX 256
+int nvfp4_quantize_grouped(const void* x, int in_dtype, int64_t T, int64_t K,
+                           const int64_t* group_rows, int64_t G, int64_t align, int64_t M_out,
+                           float bound, float* row_amax, uint8_t* q_row, uint8_t* s_row,
+                           uint8_t* q_col, uint8_t* s_col, const float* noop, void* stream);
+
 /* Dequantize one packed copy (backward-overrides PR description: the inverse
  * (scale * amax) * factor_inv with a correctly rounded FP32 reciprocal,
  * per-tensor and row-scaled, BF16 or FP32 output).

@@ -39,7 +39,10 @@ NVFP4_FLAG_FORCE_TWO_KERNEL = 1
 
 # Every entry point include/nvfp4.h declares.
 EXPORTED = ("nvfp4_amax_path", "nvfp4_amax_rowcol", "nvfp4_group_amax_expand",
-            "nvfp4_quantize_transpose", "nvfp4_dequantize", "nvfp4_status_string")
+            "nvfp4_quantize_transpose", "nvfp4_quantize_grouped", "nvfp4_dequantize",
+            "nvfp4_status_string")
+
+NVFP4_GROUPS_MAX = 256
 
 _lib = None
 
@@ -73,6 +76,9 @@ def load_library():
     lib.nvfp4_quantize_transpose.restype = c_int
     lib.nvfp4_quantize_transpose.argtypes = [vp, c_int, i64, i64, c_int, f32p, c_int, f32p, c_f,
                                              u8p, u8p, u8p, u8p, f32p, vp]
+    lib.nvfp4_quantize_grouped.restype = c_int
+    lib.nvfp4_quantize_grouped.argtypes = [vp, c_int, i64, i64, i64p, i64, i64, i64, c_f, f32p,
+                                           u8p, u8p, u8p, u8p, f32p, vp]
     lib.nvfp4_dequantize.restype = c_int
     lib.nvfp4_dequantize.argtypes = [u8p, u8p, i64, i64, c_int, f32p, c_f, vp, c_int, f32p, vp]
     _lib = lib
@@ -202,6 +208,41 @@ def nvfp4_quantize_transpose(x: torch.Tensor, row_mode: int, row_amax: Optional[
                                       _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col),
                                       _ptr(noop), _stream(stream, dev))
     _check("nvfp4_quantize_transpose", st)
+
+
+def padded_rows_max(T: int, G: int, align: int) -> int:
+    """Rows the padded layout of T tokens in G groups can need at most."""
+    return -(-(T + G * (align - 1)) // align) * align
+
+
+def nvfp4_quantize_grouped(x: torch.Tensor, group_rows: torch.Tensor, align: int, M_out: int,
+                           bound: float, row_amax: torch.Tensor,
+                           q_row: Optional[torch.Tensor], s_row: Optional[torch.Tensor],
+                           q_col: Optional[torch.Tensor], s_col: Optional[torch.Tensor],
+                           noop: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Grouped tokens x [T, K] (group sizes in the device int64 tensor
+    group_rows [G]) quantized into the padded [M_out, K] layout."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [T, K]")
+    _dev(x, "x", (torch.bfloat16, torch.float32))
+    T, K = x.shape
+    dev = x.device
+    _dev(group_rows, "group_rows", (torch.int64,), None, dev)
+    _dev(row_amax, "row_amax", _F32, M_out, dev)
+    if q_row is not None:
+        _dev(q_row, "q_row", (torch.uint8,), M_out * ((K + 1) // 2), dev)
+        _dev(s_row, "s_row", _SCALE_DTYPES, M_out * ((K + 15) // 16), dev)
+    if q_col is not None:
+        _dev(q_col, "q_col", (torch.uint8,), K * ((M_out + 1) // 2), dev)
+        _dev(s_col, "s_col", _SCALE_DTYPES, K * ((M_out + 15) // 16), dev)
+    _dev(noop, "noop", _F32, 1, dev)
+    st = lib.nvfp4_quantize_grouped(_ptr(x), _dtype_code(x), T, K, _ptr(group_rows),
+                                    group_rows.numel(), int(align), int(M_out),
+                                    ctypes.c_float(bound), _ptr(row_amax), _ptr(q_row),
+                                    _ptr(s_row), _ptr(q_col), _ptr(s_col), _ptr(noop),
+                                    _stream(stream, dev))
+    _check("nvfp4_quantize_grouped", st)
 
 
 def nvfp4_dequantize(q: torch.Tensor, sc: torch.Tensor, R: int, C: int, amax_mode: int,

@@ -305,6 +305,78 @@ __global__ void __launch_bounds__(256) group_expand_kernel(float* __restrict__ r
   for (int64_t i = s + threadIdx.x; i < e; i += 256) ra[i] = v;
 }
 
+// ------------------------------------------------------- grouped tokens
+// Grouped tokens with padding on the way in (grouped-GEMM PR description:
+// per-group global scales from the group amax, expanded to every row of the
+// padded group). Pass 1: one wave per token row that lands inside the M_out
+// padded rows computes the row's max and publishes it with atomic max into
+// the first padded row of its group (a zeroed cell); pass 2 copies that group
+// max over the group's padded rows.
+template <typename T, bool VEC>
+__global__ void __launch_bounds__(256) grouped_amax_kernel(const T* __restrict__ x, int64_t T_rows,
+                                                           int64_t K, const int64_t* grows,
+                                                           int64_t G, int64_t align, int64_t M_out,
+                                                           float* __restrict__ ra,
+                                                           const float* noop) {
+  if (skip(noop)) return;
+  __shared__ GroupTable gt;
+  build_group_table(gt, grows, G, align);
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  constexpr int V = 16 / sizeof(T);
+  const int64_t rows = min(T_rows, gt.tok0[G]);
+  for (int64_t r = wave; r < rows; r += nwaves) {
+    // padded position of the row: rows that do not fit in M_out are dropped
+    // and take no part in the group max (uniform per wave)
+    const int g = group_of(gt.tok0, (int)G, r);
+    if (gt.pad0[g] + (r - gt.tok0[g]) >= M_out) continue;
+    const T* row = x + r * K;
+    uint32_t m = 0u;
+    if (VEC) {
+      const uint4* rv = reinterpret_cast<const uint4*>(row);
+      for (int64_t i = lane; i < K / V; i += 64) {
+        const uint4 v = rv[i];
+        if constexpr (sizeof(T) == 2) {
+          const uint32_t t = pk_max_u16(pk_max_u16(v.x & kAbsBf16x2, v.y & kAbsBf16x2),
+                                        pk_max_u16(v.z & kAbsBf16x2, v.w & kAbsBf16x2));
+          m = max(m, max(t & 0xFFFFu, t >> 16) << 16);
+        } else {
+          m = max(m, max(max(v.x & kAbsF32, v.y & kAbsF32), max(v.z & kAbsF32, v.w & kAbsF32)));
+        }
+      }
+    } else {
+      for (int64_t i = lane; i < K; i += 64) {
+        if constexpr (sizeof(T) == 2)
+          m = max(m, (uint32_t)(reinterpret_cast<const uint16_t*>(row)[i] & 0x7FFFu) << 16);
+        else
+          m = max(m, reinterpret_cast<const uint32_t*>(row)[i] & kAbsF32);
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(ra + gt.pad0[g]), m);
+  }
+}
+
+// One workgroup per group: the group max (in the group's first padded row)
+// over all the group's padded rows that fit in M_out.
+__global__ void __launch_bounds__(256) grouped_expand_kernel(float* __restrict__ ra,
+                                                             const int64_t* grows, int64_t G,
+                                                             int64_t align, int64_t M_out,
+                                                             const float* noop) {
+  if (skip(noop)) return;
+  __shared__ GroupTable gt;
+  __shared__ float gmax;
+  build_group_table(gt, grows, G, align);
+  const int g = blockIdx.x;
+  const int64_t s = gt.pad0[g], e = min(gt.pad0[g + 1], M_out);
+  if (s >= e) return;  // empty group, or past M_out (uniform per workgroup)
+  if (threadIdx.x == 0) gmax = ra[s];
+  __syncthreads();
+  const float v = gmax;
+  for (int64_t i = s + threadIdx.x; i < e; i += 256) ra[i] = v;
+}
+
 // ================================================================ launchers
 
 int launch_amax_init(float* ra, int64_t M, float* ca, int64_t K, float* ta, const float* noop,
@@ -390,6 +462,38 @@ int launch_tensor_amax(const void* x, int in_dtype, int64_t n, float* ta, const 
 int launch_group_expand(float* ra, int64_t M, const int64_t* group_end, int64_t G,
                         const float* noop, hipStream_t s) {
   hipLaunchKernelGGL(group_expand_kernel, dim3((unsigned)G), dim3(256), 0, s, ra, M, group_end, noop);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // namespace nvfp4
+
+namespace nvfp4 {
+
+int launch_grouped_amax(const void* x, int in_dtype, int64_t T, int64_t K, const int64_t* grows,
+                        int64_t G, int64_t align, int64_t M_out, float* ra, const float* noop,
+                        hipStream_t s) {
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((T + 3) / 4, (int64_t)num_cus() * 16));
+  const bool vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  if (in_dtype == 0) {
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    if (vec16 && K % 8 == 0)
+      hipLaunchKernelGGL((grouped_amax_kernel<uint16_t, true>), dim3((unsigned)blocks), dim3(256), 0, s,
+                         xb, T, K, grows, G, align, M_out, ra, noop);
+    else
+      hipLaunchKernelGGL((grouped_amax_kernel<uint16_t, false>), dim3((unsigned)blocks), dim3(256), 0, s,
+                         xb, T, K, grows, G, align, M_out, ra, noop);
+  } else {
+    const float* xf = static_cast<const float*>(x);
+    if (vec16 && K % 4 == 0)
+      hipLaunchKernelGGL((grouped_amax_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0, s,
+                         xf, T, K, grows, G, align, M_out, ra, noop);
+    else
+      hipLaunchKernelGGL((grouped_amax_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0, s,
+                         xf, T, K, grows, G, align, M_out, ra, noop);
+  }
+  if (hipGetLastError() != hipSuccess) return -3;
+  hipLaunchKernelGGL(grouped_expand_kernel, dim3((unsigned)G), dim3(256), 0, s, ra, grows, G, align,
+                     M_out, noop);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

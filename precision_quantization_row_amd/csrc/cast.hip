@@ -59,6 +59,10 @@ struct CastK {
   // seg0 + b / nstrips of strip strip0 + b % nstrips
   int64_t rstart, rend, rows_per_wg;
   int64_t seg0, strip0, nstrips;
+  // grouped tokens (edge kernel only): output row r reads token row
+  // token_row(r) of x, or is a zero row
+  const int64_t* grp_rows;
+  int64_t grp_G, grp_align, grp_T;
 };
 
 // Lane block storage: NW dwords per row. BF16: 4 dwords = 8 values (element
@@ -732,7 +736,10 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
   constexpr int NW = Blk<T>::NW;
   __shared__ float row_a_s[CAST_MAX_ROWS_PER_WG];
   __shared__ float row_se_s[CAST_MAX_ROWS_PER_WG];
+  __shared__ GroupTable gt;
   const T* __restrict__ x = static_cast<const T*>(p.x);
+  const bool grouped = p.grp_G > 0;  // uniform
+  if (grouped) build_group_table(gt, p.grp_rows, p.grp_G, p.grp_align);
   const int tid = threadIdx.x;
   const int wv = tid >> 6;
   const int lane = tid & 63;
@@ -792,7 +799,15 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
     const int64_t rb0 = r0 + 16 * g;
     uint32_t w[16][NW];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) load_row_checked<T>(x, re, K, rb0 + i, c, vec, w[i]);
+    for (int i = 0; i < 16; ++i) {
+      if (grouped) {  // padding rows and rows past the groups read as zeros
+        const int64_t rr = rb0 + i;
+        const int64_t src = rr < re ? token_row(gt, (int)p.grp_G, rr) : -1;
+        load_row_checked<T>(x, p.grp_T, K, src < 0 ? p.grp_T : src, c, vec, w[i]);
+      } else {
+        load_row_checked<T>(x, re, K, rb0 + i, c, vec, w[i]);
+      }
+    }
     st.rb0 = rb0;
     if constexpr (COLW) {
       if (p.col_mode == 2) {
@@ -884,6 +899,10 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
   k.q_col = a.q_col;
   k.s_col = a.s_col;
   k.noop = a.noop;
+  k.grp_rows = a.grp_rows;
+  k.grp_G = a.grp_G;
+  k.grp_align = a.grp_align;
+  k.grp_T = a.grp_T;
   constexpr int V = 16 / sizeof(T);
   k.vec_load = ((a.K % V) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
   k.row_store4 = (a.K % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0);
@@ -896,7 +915,7 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
   const int64_t lim = 0x7FFFFFFF;
   const int64_t scs = (a.M + 15) / 16;
   const uintptr_t sc_align = (scs % 16 == 0) ? 15 : 3;
-  const bool fast = k.vec_load && (a.K % IT_COLS == 0) && (a.M % 64 == 0) &&
+  const bool fast = a.grp_G == 0 && k.vec_load && (a.K % IT_COLS == 0) && (a.M % 64 == 0) &&
                     (!a.q_row || (reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0) &&
                     (!a.s_row || (reinterpret_cast<uintptr_t>(a.s_row) & 15) == 0) &&
                     (!a.q_col || (reinterpret_cast<uintptr_t>(a.q_col) & 15) == 0) &&

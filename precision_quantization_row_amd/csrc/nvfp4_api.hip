@@ -127,6 +127,50 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
   return launch_cast(a, static_cast<hipStream_t>(stream)) ? NVFP4_ERR_HIP : NVFP4_OK;
 }
 
+int nvfp4_quantize_grouped(const void* x, int in_dtype, int64_t T, int64_t K,
+                           const int64_t* group_rows, int64_t G, int64_t align, int64_t M_out,
+                           float bound, float* row_amax, uint8_t* q_row, uint8_t* s_row,
+                           uint8_t* q_col, uint8_t* s_col, const float* noop, void* stream) {
+  if (x == nullptr || group_rows == nullptr || row_amax == nullptr) return NVFP4_ERR_ARG;
+  if (T < 1 || K < 1 || M_out < 1) return NVFP4_ERR_ARG;
+  if (T > (int64_t)1 << 40 || K > (int64_t)1 << 40 || M_out > (int64_t)1 << 40) return NVFP4_ERR_ARG;
+  if (in_dtype != NVFP4_BF16 && in_dtype != NVFP4_FP32) return NVFP4_ERR_ARG;
+  if (G < 1) return NVFP4_ERR_ARG;
+  if (G > NVFP4_GROUPS_MAX) return NVFP4_ERR_UNSUPPORTED;
+  if (align < 16 || align > 4096 || align % 16 != 0) return NVFP4_ERR_ARG;
+  if (!valid_bound(bound)) return NVFP4_ERR_ARG;
+  const bool rw = q_row != nullptr || s_row != nullptr;
+  const bool cw = q_col != nullptr || s_col != nullptr;
+  if (!rw && !cw) return NVFP4_ERR_ARG;
+  if (rw && (!q_row || !s_row)) return NVFP4_ERR_ARG;
+  if (cw && (!q_col || !s_col)) return NVFP4_ERR_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_amax_init(row_amax, M_out, nullptr, 0, nullptr, noop, s)) return NVFP4_ERR_HIP;
+  if (launch_grouped_amax(x, in_dtype, T, K, group_rows, G, align, M_out, row_amax, noop, s))
+    return NVFP4_ERR_HIP;
+  CastArgs a;
+  a.x = x;
+  a.in_dtype = in_dtype;
+  a.M = M_out;
+  a.K = K;
+  a.row_mode = NVFP4_AMAX_LINE;
+  a.row_amax = row_amax;
+  a.col_mode = NVFP4_AMAX_ROWGROUP;
+  a.col_amax = row_amax;
+  a.F = bound * 6.0f;
+  a.F_inv = 1.0f / a.F;
+  a.q_row = rw ? q_row : nullptr;
+  a.s_row = rw ? s_row : nullptr;
+  a.q_col = cw ? q_col : nullptr;
+  a.s_col = cw ? s_col : nullptr;
+  a.noop = noop;
+  a.grp_rows = group_rows;
+  a.grp_G = G;
+  a.grp_align = align;
+  a.grp_T = T;
+  return launch_cast(a, s) ? NVFP4_ERR_HIP : NVFP4_OK;
+}
+
 int nvfp4_dequantize(const uint8_t* q, const uint8_t* sc, int64_t R, int64_t C, int amax_mode,
                      const float* amax, float bound, void* y, int out_dtype, const float* noop,
                      void* stream) {

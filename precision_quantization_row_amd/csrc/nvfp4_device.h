@@ -141,4 +141,62 @@ __device__ __forceinline__ uint32_t e2m1_pack8(float v0, float v1, float v2, flo
   return w;
 }
 
+// -------------------------------------------------------- grouped tokens
+// Ragged token groups laid out padded (grouped-GEMM PR description: groups
+// zero-padded to an alignment before quantization): group g holds rows[g]
+// consecutive token rows starting at tok0[g] and occupies the padded rows
+// [pad0[g], pad0[g + 1]), its size rounded up to `align`. Both prefix sums
+// live in LDS; every workgroup of 256 threads builds them itself (G <= 256).
+constexpr int GRP_MAX = 256;
+
+struct GroupTable {
+  int64_t tok0[GRP_MAX + 1];
+  int64_t pad0[GRP_MAX + 1];
+};
+
+// Inclusive scan of the sizes (negative sizes count as 0); all 256 threads.
+__device__ __forceinline__ void build_group_table(GroupTable& gt, const int64_t* rows, int64_t G,
+                                                  int64_t align) {
+  const int t = threadIdx.x;
+  const int64_t n = (t < G) ? max(rows[t], (int64_t)0) : 0;
+  gt.tok0[t + 1] = n;
+  gt.pad0[t + 1] = (n + align - 1) / align * align;
+  if (t == 0) gt.tok0[0] = gt.pad0[0] = 0;
+  __syncthreads();
+  for (int off = 1; off < GRP_MAX; off <<= 1) {
+    int64_t a = 0, b = 0;
+    if (t >= off) {
+      a = gt.tok0[t + 1 - off];
+      b = gt.pad0[t + 1 - off];
+    }
+    __syncthreads();
+    if (t >= off) {
+      gt.tok0[t + 1] += a;
+      gt.pad0[t + 1] += b;
+    }
+    __syncthreads();
+  }
+}
+
+// The group holding v, for starts[0] <= v < starts[G]: the last g with
+// starts[g] <= v (empty groups share their start with the next group).
+__device__ __forceinline__ int group_of(const int64_t* starts, int G, int64_t v) {
+  int lo = 0, hi = G;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (starts[mid] <= v) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Token row behind padded row pr, or -1 for a padding row (or a row past the
+// last group).
+__device__ __forceinline__ int64_t token_row(const GroupTable& gt, int G, int64_t pr) {
+  if (pr < 0 || pr >= gt.pad0[G]) return -1;
+  const int g = group_of(gt.pad0, G, pr);
+  const int64_t r = pr - gt.pad0[g];
+  return r < gt.tok0[g + 1] - gt.tok0[g] ? gt.tok0[g] + r : -1;
+}
+
 }  // namespace nvfp4

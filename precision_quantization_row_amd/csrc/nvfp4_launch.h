@@ -21,6 +21,11 @@ int launch_tensor_amax(const void* x, int in_dtype, int64_t n, float* ta, const 
                        hipStream_t s);
 int launch_group_expand(float* ra, int64_t M, const int64_t* group_end, int64_t G,
                         const float* noop, hipStream_t s);
+// grouped tokens: group amax of each token group into the first padded row of
+// the group (ra zeroed beforehand), then expanded over the padded group
+int launch_grouped_amax(const void* x, int in_dtype, int64_t T, int64_t K, const int64_t* grows,
+                        int64_t G, int64_t align, int64_t M_out, float* ra, const float* noop,
+                        hipStream_t s);
 
 struct CastArgs {
   const void* x;
@@ -33,6 +38,10 @@ struct CastArgs {
   float F, F_inv;
   uint8_t *q_row, *s_row, *q_col, *s_col;
   const float* noop;
+  // grouped tokens (grp_G > 0): x holds grp_T token rows; output row r is
+  // token row token_row(r) or a zero row (padding)
+  const int64_t* grp_rows = nullptr;
+  int64_t grp_G = 0, grp_align = 16, grp_T = 0;
 };
 int launch_cast(const CastArgs& a, hipStream_t s);
 

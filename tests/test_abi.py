@@ -97,6 +97,16 @@ def test_validation_rejects_before_launch():
     assert d(bound=500.0) == E
     assert d(R=0) == E
     assert d(C=0) == E
+    # grouped tokens: sizes, group count, alignment, bound, missing buffers
+    g = lambda T=64, K=32, G=4, align=16, M=128, bound=448.0, x=_fake(), gr=_fake(), ra=_fake(), \
+        qr=_fake(), sr=_fake(), qc=_fake(), sc=_fake(), dt=0: lib.nvfp4_quantize_grouped(
+            x, dt, T, K, gr, G, align, M, f(bound), ra, qr, sr, qc, sc, None, None)
+    for kw in (dict(T=0), dict(K=0), dict(M=0), dict(G=0), dict(align=8), dict(align=24),
+               dict(align=8192), dict(bound=0.0), dict(bound=500.0), dict(x=None), dict(gr=None),
+               dict(ra=None), dict(dt=3), dict(qr=None, sr=None, qc=None, sc=None),
+               dict(sr=None), dict(qc=None)):
+        assert g(**kw) == E, kw
+    assert g(G=p.NVFP4_GROUPS_MAX + 1) == p.NVFP4_ERR_UNSUPPORTED
     # group expansion
     assert lib.nvfp4_group_amax_expand(_fake(), 16, _fake(), 0, None, None) == E
     assert lib.nvfp4_group_amax_expand(None, 16, _fake(), 2, None, None) == E
