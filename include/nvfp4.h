@@ -155,7 +155,8 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
  *   q_col [K][ceil(M_out/2)], s_col [K][ceil(M_out/16)] (both or neither):
  *              rowwise codes with the per-row amax, transposed codes with
  *              the group amax of each 16-row block (as mode ROWGROUP)
- * At least one copy must be requested. */
+ * At least one copy must be requested. T and M_out must be below 2^31 - 1
+ * (NVFP4_ERR_UNSUPPORTED otherwise). */
 #define NVFP4_GROUPS_MAX 256
 int nvfp4_quantize_grouped(const void* x, int in_dtype, int64_t T, int64_t K,
                            const int64_t* group_rows, int64_t G, int64_t align, int64_t M_out,

@@ -308,29 +308,32 @@ __global__ void __launch_bounds__(256) group_expand_kernel(float* __restrict__ r
 // ------------------------------------------------------- grouped tokens
 // Grouped tokens with padding on the way in (grouped-GEMM PR description:
 // per-group global scales from the group amax, expanded to every row of the
-// padded group). Pass 1: one wave per token row that lands inside the M_out
-// padded rows computes the row's max and publishes it with atomic max into
-// the first padded row of its group (a zeroed cell); pass 2 copies that group
-// max over the group's padded rows.
+// padded group). Pass 1: one wave per token row writes the row's max into the
+// padded row the token lands in (a row that does not fit in M_out is
+// skipped). Pass 2: one workgroup per group reduces those row maxima and
+// writes the group max over the group's padded rows; the workgroups past the
+// last group write 0 over the rows past it. Every row of [0, M_out) is
+// written once, so nothing has to be zeroed first. T, M_out < 2^31.
 template <typename T, bool VEC>
-__global__ void __launch_bounds__(256) grouped_amax_kernel(const T* __restrict__ x, int64_t T_rows,
-                                                           int64_t K, const int64_t* grows,
-                                                           int64_t G, int64_t align, int64_t M_out,
-                                                           float* __restrict__ ra,
-                                                           const float* noop) {
+__global__ void __launch_bounds__(256) grouped_row_amax_kernel(const T* __restrict__ x,
+                                                               int64_t T_rows, int64_t K,
+                                                               const int64_t* grows, int G,
+                                                               int64_t align, int64_t M_out,
+                                                               float* __restrict__ ra,
+                                                               const float* noop) {
   if (skip(noop)) return;
-  __shared__ GroupTable gt;
-  build_group_table(gt, grows, G, align);
   const int lane = threadIdx.x & 63;
+  const LaneEnds e = lane_group_ends(grows, G, align, lane);
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   constexpr int V = 16 / sizeof(T);
-  const int64_t rows = min(T_rows, gt.tok0[G]);
-  for (int64_t r = wave; r < rows; r += nwaves) {
-    // padded position of the row: rows that do not fit in M_out are dropped
-    // and take no part in the group max (uniform per wave)
-    const int g = group_of(gt.tok0, (int)G, r);
-    if (gt.pad0[g] + (r - gt.tok0[g]) >= M_out) continue;
+  for (int64_t r = wave; r < T_rows; r += nwaves) {
+    const uint32_t g = groups_ending_by(e.tok, (uint32_t)r);
+    if (g >= (uint32_t)G) break;  // this and every later row lie past the groups
+    const uint32_t t0 = g ? group_end_at(e.tok, g - 1) : 0u;
+    const uint32_t p0 = g ? group_end_at(e.pad, g - 1) : 0u;
+    const int64_t pr = (int64_t)p0 + (r - (int64_t)t0);
+    if (pr >= M_out) continue;
     const T* row = x + r * K;
     uint32_t m = 0u;
     if (VEC) {
@@ -354,27 +357,42 @@ __global__ void __launch_bounds__(256) grouped_amax_kernel(const T* __restrict__
       }
     }
     for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(ra + gt.pad0[g]), m);
+    if (lane == 0) ra[pr] = __uint_as_float(m);
   }
 }
 
-// One workgroup per group: the group max (in the group's first padded row)
-// over all the group's padded rows that fit in M_out.
+// Workgroup g < G: group g. Its token rows that exist (below T) and fit in
+// M_out carry their row maxima from pass 1; their max goes over every padded
+// row of the group that fits. Workgroups G .. grid - 1: zeros over
+// [P_G, M_out), P_G = the padded end of the last group.
 __global__ void __launch_bounds__(256) grouped_expand_kernel(float* __restrict__ ra,
-                                                             const int64_t* grows, int64_t G,
-                                                             int64_t align, int64_t M_out,
-                                                             const float* noop) {
+                                                             const int64_t* grows, int G,
+                                                             int64_t align, int64_t T_rows,
+                                                             int64_t M_out, const float* noop) {
   if (skip(noop)) return;
-  __shared__ GroupTable gt;
-  __shared__ float gmax;
-  build_group_table(gt, grows, G, align);
-  const int g = blockIdx.x;
-  const int64_t s = gt.pad0[g], e = min(gt.pad0[g + 1], M_out);
-  if (s >= e) return;  // empty group, or past M_out (uniform per workgroup)
-  if (threadIdx.x == 0) gmax = ra[s];
+  __shared__ uint32_t wmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const LaneEnds e = lane_group_ends(grows, G, align, lane);
+  const int64_t PG = group_end_at(e.pad, (uint32_t)G - 1);
+  if ((int)blockIdx.x >= G) {
+    const int64_t n = (int64_t)gridDim.x - G;
+    for (int64_t i = PG + ((int64_t)blockIdx.x - G) * 256 + tid; i < M_out; i += n * 256) ra[i] = 0.0f;
+    return;
+  }
+  const uint32_t g = blockIdx.x;
+  const int64_t t0 = g ? group_end_at(e.tok, g - 1) : 0u, t1 = group_end_at(e.tok, g);
+  const int64_t p0 = g ? group_end_at(e.pad, g - 1) : 0u, p1 = group_end_at(e.pad, g);
+  const int64_t pe = min(p1, M_out);
+  if (p0 >= pe) return;  // empty group, or past M_out (uniform per workgroup)
+  // rows of the group written by pass 1
+  const int64_t n = min(min(t1, T_rows) - t0, pe - p0);
+  uint32_t m = 0u;
+  for (int64_t i = tid; i < n; i += 256) m = max(m, __float_as_uint(ra[p0 + i]));
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if (lane == 0) wmax[wv] = m;
   __syncthreads();
-  const float v = gmax;
-  for (int64_t i = s + threadIdx.x; i < e; i += 256) ra[i] = v;
+  const float v = __uint_as_float(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3])));
+  for (int64_t i = p0 + tid; i < pe; i += 256) ra[i] = v;
 }
 
 // ================================================================ launchers
@@ -474,26 +492,29 @@ int launch_grouped_amax(const void* x, int in_dtype, int64_t T, int64_t K, const
                         hipStream_t s) {
   const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((T + 3) / 4, (int64_t)num_cus() * 16));
   const bool vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  const int g = (int)G;
   if (in_dtype == 0) {
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     if (vec16 && K % 8 == 0)
-      hipLaunchKernelGGL((grouped_amax_kernel<uint16_t, true>), dim3((unsigned)blocks), dim3(256), 0, s,
-                         xb, T, K, grows, G, align, M_out, ra, noop);
+      hipLaunchKernelGGL((grouped_row_amax_kernel<uint16_t, true>), dim3((unsigned)blocks), dim3(256),
+                         0, s, xb, T, K, grows, g, align, M_out, ra, noop);
     else
-      hipLaunchKernelGGL((grouped_amax_kernel<uint16_t, false>), dim3((unsigned)blocks), dim3(256), 0, s,
-                         xb, T, K, grows, G, align, M_out, ra, noop);
+      hipLaunchKernelGGL((grouped_row_amax_kernel<uint16_t, false>), dim3((unsigned)blocks), dim3(256),
+                         0, s, xb, T, K, grows, g, align, M_out, ra, noop);
   } else {
     const float* xf = static_cast<const float*>(x);
     if (vec16 && K % 4 == 0)
-      hipLaunchKernelGGL((grouped_amax_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0, s,
-                         xf, T, K, grows, G, align, M_out, ra, noop);
+      hipLaunchKernelGGL((grouped_row_amax_kernel<float, true>), dim3((unsigned)blocks), dim3(256), 0,
+                         s, xf, T, K, grows, g, align, M_out, ra, noop);
     else
-      hipLaunchKernelGGL((grouped_amax_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0, s,
-                         xf, T, K, grows, G, align, M_out, ra, noop);
+      hipLaunchKernelGGL((grouped_row_amax_kernel<float, false>), dim3((unsigned)blocks), dim3(256), 0,
+                         s, xf, T, K, grows, g, align, M_out, ra, noop);
   }
   if (hipGetLastError() != hipSuccess) return -3;
-  hipLaunchKernelGGL(grouped_expand_kernel, dim3((unsigned)G), dim3(256), 0, s, ra, grows, G, align,
-                     M_out, noop);
+  // G group workgroups + enough for the zero tail (at most M_out rows)
+  const int64_t tail = std::min<int64_t>((M_out + 255) / 256, (int64_t)num_cus() * 2);
+  hipLaunchKernelGGL(grouped_expand_kernel, dim3((unsigned)(G + tail)), dim3(256), 0, s, ra, grows, g,
+                     align, T, M_out, noop);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

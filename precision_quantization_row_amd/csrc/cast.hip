@@ -59,8 +59,8 @@ struct CastK {
   // seg0 + b / nstrips of strip strip0 + b % nstrips
   int64_t rstart, rend, rows_per_wg;
   int64_t seg0, strip0, nstrips;
-  // grouped tokens (edge kernel only): output row r reads token row
-  // token_row(r) of x, or is a zero row
+  // grouped tokens (grp_G > 0): x holds grp_T token rows; output row r reads
+  // token row token_row(r) of x, or is a zero row (padding, past the groups)
   const int64_t* grp_rows;
   int64_t grp_G, grp_align, grp_T;
 };
@@ -512,8 +512,11 @@ struct ITSmem {
   uint8_t sr[2][IT_SUB][16];
   // per-wave row amax / S_enc of the wave's 32 rows
   float ra[4][32], rs[4][32];
-  // column amax / S_enc of the strip's 256 columns
-  float ca[IT_COLS], cs[IT_COLS];
+  // column amax / S_enc of the strip's 256 columns (modes 0 and 1); grouped
+  // tokens use mode 2 and keep their group table here instead: gtok[g] and
+  // gpad[g] are the ends of group g in token rows and in padded rows
+  union { float ca[IT_COLS]; uint32_t gtok[IT_COLS]; };
+  union { float cs[IT_COLS]; uint32_t gpad[IT_COLS]; };
   // row-group mode: the group amax / S_enc of each wave half's 16-row block,
   // repeated for the lane's 8 columns
   float ga[4][2][8], gs[4][2][8];
@@ -544,7 +547,87 @@ struct StoreIT {
   }
 };
 
-template <typename T, bool ROWW, bool COLW>
+// Grouped tokens in the interior kernel. The group table is built once per
+// workgroup in 32-bit form: inclusive prefix sums of the group sizes in token
+// rows (gtok) and rounded up to the alignment in padded rows (gpad), both
+// saturating at 2^31 - 1 (the host sends only T, M < 2^31 here, so a
+// saturated end lies past every row the kernel touches); entries from G on
+// hold 0xFFFFFFFF in gpad. All 256 threads.
+__device__ __forceinline__ void build_group_table32(ITSmem& sm, const int64_t* rows, int G,
+                                                    int64_t align) {
+  constexpr uint32_t CL = 0x7FFFFFFFu;
+  const int t = threadIdx.x;
+  const int64_t n = t < G ? min(max(rows[t], (int64_t)0), (int64_t)CL) : 0;
+  sm.gtok[t] = (uint32_t)n;
+  sm.gpad[t] = (uint32_t)min((n + align - 1) / align * align, (int64_t)CL);
+  __syncthreads();
+  for (int off = 1; off < IT_COLS; off <<= 1) {
+    uint32_t a = 0u, b = 0u;
+    if (t >= off) {
+      a = sm.gtok[t - off];
+      b = sm.gpad[t - off];
+    }
+    __syncthreads();
+    if (t >= off) {
+      sm.gtok[t] = min(sm.gtok[t] + a, CL);
+      sm.gpad[t] = min(sm.gpad[t] + b, CL);
+    }
+    __syncthreads();
+  }
+  if (t >= G) sm.gpad[t] = 0xFFFFFFFFu;
+  __syncthreads();
+}
+
+// Where a wave's 32 padded rows pr0 .. pr0 + 31 come from (pr0 a multiple of
+// 16; the alignment is one too, so each 16-row half lies in one group or past
+// the last). Half h is n[h] consecutive token rows, then zero rows. The two
+// halves lie within 32 token rows of `base`: half 0 at base, half 1 at
+// base + d1 (0 <= d1 <= 16: when both halves hold tokens, half 0 is 16 rows of
+// its group or that group's last rows, and the tokens of half 1 follow).
+// lim = token rows from base that the buffer may read (at most 32, never past
+// T). Every value is wave-uniform; all 64 lanes must be active.
+struct WaveRows {
+  int64_t base;
+  uint32_t lim, d1, n0, n1;
+};
+
+__device__ __forceinline__ WaveRows grouped_wave_rows(const ITSmem& sm, int G, uint32_t T,
+                                                      int lane, uint32_t pr0) {
+  // group of a padded row = the number of groups that end at or before it
+  const u32x4 e = *reinterpret_cast<const u32x4*>(&sm.gpad[4 * lane]);
+  const uint32_t pr1 = pr0 + 16u;
+  const uint32_t g0 = __builtin_popcountll(__builtin_amdgcn_ballot_w64(e.x <= pr0)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(e.y <= pr0)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(e.z <= pr0)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(e.w <= pr0));
+  const uint32_t g1 = __builtin_popcountll(__builtin_amdgcn_ballot_w64(e.x <= pr1)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(e.y <= pr1)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(e.z <= pr1)) +
+                      __builtin_popcountll(__builtin_amdgcn_ballot_w64(e.w <= pr1));
+  auto half = [&](uint32_t g, uint32_t pr, uint32_t& src, uint32_t& n) {
+    src = 0u;
+    n = 0u;
+    if (g >= (uint32_t)G) return;  // past the last group: zero rows
+    const uint32_t sp = g ? __builtin_amdgcn_readfirstlane(sm.gpad[g - 1]) : 0u;
+    const uint32_t st = g ? __builtin_amdgcn_readfirstlane(sm.gtok[g - 1]) : 0u;
+    const uint32_t et = __builtin_amdgcn_readfirstlane(sm.gtok[g]);
+    src = st + (pr - sp);
+    n = src < et ? min(et - src, 16u) : 0u;
+    n = src < T ? min(n, T - src) : 0u;
+  };
+  uint32_t s0, n0, s1, n1;
+  half(g0, pr0, s0, n0);
+  half(g1, pr1, s1, n1);
+  WaveRows w;
+  w.base = n0 ? s0 : (n1 ? s1 : 0u);
+  w.d1 = (n0 && n1) ? s1 - s0 : 0u;
+  w.n0 = n0;
+  w.n1 = n1;
+  w.lim = (uint32_t)min((int64_t)32, max((int64_t)T - w.base, (int64_t)0));
+  return w;
+}
+
+template <typename T, bool ROWW, bool COLW, bool GRP>
 __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_kernel(const CastK p) {
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   constexpr int NW = Blk<T>::NW;
@@ -590,24 +673,51 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
   auto wave_rows = [&](int64_t rs, int64_t c0) {
     return make_rsrc(x + (rs + 32 * wv) * K + c0, (int64_t)32 * K * (int64_t)sizeof(T));
   };
+  // grouped tokens: the rows of a sub-step come through a WaveRows map; a
+  // lane's row i past its half's n rows gets an offset beyond the buffer's
+  // range, which reads as zero
+  if constexpr (GRP) build_group_table32(sm, p.grp_rows, (int)p.grp_G, p.grp_align);
+  const uint32_t grp_T = (uint32_t)p.grp_T;
+  auto grp_map = [&](int64_t rs) { return grouped_wave_rows(sm, (int)p.grp_G, grp_T, lane, (uint32_t)(rs + 32 * wv)); };
+  auto grp_rsrc = [&](const WaveRows& m, int64_t c0) {
+    return make_rsrc(x + m.base * K + c0, (int64_t)m.lim * K * (int64_t)sizeof(T));
+  };
+  auto grp_vo = [&](const WaveRows& m) {
+    return (h ? m.d1 * rowbytes : 0u) + (uint32_t)(8 * L * sizeof(T));
+  };
+  auto grp_load = [&](const __amdgpu_buffer_rsrc_t& r, uint32_t v, uint32_t n, int i,
+                      uint32_t (&out)[NW]) {
+    load_row_buf<T>(r, (uint32_t)i < n ? v : 0x80000000u, (uint32_t)i * rowbytes, out);
+  };
   // The first PF rows of each half of the wave's next sub-step are loaded while
   // the current one's block scales and codes are computed (BF16: 32 registers;
   // FP32 has none to spare). Loading all 16 rows ahead needs 32 more registers
   // than a wave has at 2 waves per SIMD and ends up slower.
   constexpr int PF = sizeof(T) == 2 ? 8 : 0;
   uint32_t pf[PF > 0 ? PF : 1][NW];
-  auto prefetch = [&](int64_t rs, int64_t c0) {
+  auto prefetch = [&](int64_t rs, int64_t c0, WaveRows m) {
     if constexpr (PF > 0) {
-      const __amdgpu_buffer_rsrc_t rn = wave_rows(rs, c0);
+      if constexpr (GRP) {
+        const __amdgpu_buffer_rsrc_t rn = grp_rsrc(m, c0);
+        const uint32_t gv = grp_vo(m), gn = h ? m.n1 : m.n0;
 #pragma unroll
-      for (int i = 0; i < PF; ++i) load_row_buf<T>(rn, vo, (uint32_t)i * rowbytes, pf[i]);
+        for (int i = 0; i < PF; ++i) grp_load(rn, gv, gn, i, pf[i]);
+      } else {
+        const __amdgpu_buffer_rsrc_t rn = wave_rows(rs, c0);
+#pragma unroll
+        for (int i = 0; i < PF; ++i) load_row_buf<T>(rn, vo, (uint32_t)i * rowbytes, pf[i]);
+      }
     }
   };
 
   int sbuf = 0, mbuf = 0;
   int64_t m0 = 0, c0 = 0, c0_tab = -1;
   int64_t v = next_sub(0, m0, c0);
-  if (v < n_v) prefetch(m0 + (v & 1) * IT_SUB, c0);
+  WaveRows gm{0, 0u, 0u, 0u, 0u};  // grouped: the current sub-step's rows
+  if constexpr (GRP) {
+    if (v < n_v) gm = grp_map(m0 + (v & 1) * IT_SUB);
+  }
+  if (v < n_v) prefetch(m0 + (v & 1) * IT_SUB, c0, gm);
   while (v < n_v) {
     const int sub = (int)(v & 1);
     const int64_t rs = m0 + sub * IT_SUB;
@@ -616,7 +726,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     // (mode 2)
     ColLds ctab{&sm.ca[8 * L], &sm.cs[8 * L]};
     if constexpr (COLW) {
-      if (p.col_mode == 2) {
+      if (GRP || p.col_mode == 2) {
         if (L < 8) {
           const float a = p.col_amax[rs + 32 * wv + 16 * h];
           sm.ga[wv][h][L] = a;
@@ -643,7 +753,19 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
       __builtin_amdgcn_wave_barrier();
     }
     uint32_t w[16][NW];
-    {
+    if constexpr (GRP) {
+      const __amdgpu_buffer_rsrc_t rx = grp_rsrc(gm, c0);
+      const uint32_t gv = grp_vo(gm), gn = h ? gm.n1 : gm.n0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < PF) {
+#pragma unroll
+          for (int d = 0; d < NW; ++d) w[i][d] = pf[i < PF ? i : 0][d];
+        } else {
+          grp_load(rx, gv, gn, i, w[i]);
+        }
+      }
+    } else {
       const __amdgpu_buffer_rsrc_t rx = wave_rows(rs, c0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -657,6 +779,10 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     }
     int64_t m0n = 0, c0n = 0;
     const int64_t vn = next_sub(v + 1, m0n, c0n);
+    WaveRows gmn{0, 0u, 0u, 0u, 0u};
+    if constexpr (GRP) {
+      if (vn < n_v) gmn = grp_map(m0n + (vn & 1) * IT_SUB);
+    }
 
     StoreIT st;
     st.wv = wv;
@@ -673,7 +799,11 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
       st.vo_qr = (uint32_t)h * 16u * (uint32_t)qrs + (uint32_t)(4 * L);
     }
     auto mid = [&]() {
-      if (vn < n_v) prefetch(m0n + (vn & 1) * IT_SUB, c0n);
+      if constexpr (GRP) {
+        if (vn < n_v) prefetch(m0n + (vn & 1) * IT_SUB, c0n, gmn);
+      } else {
+        if (vn < n_v) prefetch(m0n + (vn & 1) * IT_SUB, c0n, WaveRows{0, 0u, 0u, 0u, 0u});
+      }
     };
     process_block_batched<T, ROWW, COLW>(w, st, h, par, LdsTab{sm.ra[wv], sm.rs[wv], 0}, ctab,
                                          p.F_inv, mid);
@@ -721,6 +851,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     v = vn;
     m0 = m0n;
     c0 = c0n;
+    if constexpr (GRP) gm = gmn;
   }
 }
 
@@ -825,7 +956,7 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
   }
 }
 
-template <typename T, bool ROWW, bool COLW>
+template <typename T, bool ROWW, bool COLW, bool GRP>
 static int interior_grid() {
   // resident interior workgroups on the device (a multiple of 8), per device
   static int cache[64] = {0};
@@ -834,7 +965,7 @@ static int interior_grid() {
   if (cache[dev] == 0) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW>), 256, 0) !=
+            &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW, GRP>), 256, 0) !=
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
@@ -850,9 +981,15 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
   if (ntiles > 0) {
     // all resident workgroups: a partly idle last round costs less than
     // fewer waves per CU
-    const int64_t G = interior_grid<T, ROWW, COLW>();
-    hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW>), dim3((unsigned)G), dim3(256), 0, s,
-                       k);
+    if (k.grp_G > 0) {
+      const int64_t G = interior_grid<T, ROWW, COLW, true>();
+      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, true>), dim3((unsigned)G), dim3(256),
+                         0, s, k);
+    } else {
+      const int64_t G = interior_grid<T, ROWW, COLW, false>();
+      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, false>), dim3((unsigned)G), dim3(256),
+                         0, s, k);
+    }
   }
   // edge rectangles: (1) the partial last strip over all rows,
   // (2) the rows below the interior for the full strips
@@ -915,7 +1052,12 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
   const int64_t lim = 0x7FFFFFFF;
   const int64_t scs = (a.M + 15) / 16;
   const uintptr_t sc_align = (scs % 16 == 0) ? 15 : 3;
-  const bool fast = a.grp_G == 0 && k.vec_load && (a.K % IT_COLS == 0) && (a.M % 64 == 0) &&
+  // Grouped tokens (always row mode LINE, column mode ROWGROUP) take the
+  // interior path too when token rows and padded rows index in 31 bits (a
+  // masked row's offset, 2^31 + 15 rows, then stays within 32 bits).
+  const bool grp_ok = a.grp_G == 0 || (a.grp_G <= IT_COLS && a.row_mode == 1 && a.col_mode == 2 &&
+                                       a.grp_T < lim && a.M < lim);
+  const bool fast = grp_ok && k.vec_load && (a.K % IT_COLS == 0) && (a.M % 64 == 0) &&
                     (!a.q_row || (reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0) &&
                     (!a.s_row || (reinterpret_cast<uintptr_t>(a.s_row) & 15) == 0) &&
                     (!a.q_col || (reinterpret_cast<uintptr_t>(a.q_col) & 15) == 0) &&

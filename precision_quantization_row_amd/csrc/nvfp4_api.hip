@@ -134,6 +134,7 @@ int nvfp4_quantize_grouped(const void* x, int in_dtype, int64_t T, int64_t K,
   if (x == nullptr || group_rows == nullptr || row_amax == nullptr) return NVFP4_ERR_ARG;
   if (T < 1 || K < 1 || M_out < 1) return NVFP4_ERR_ARG;
   if (T > (int64_t)1 << 40 || K > (int64_t)1 << 40 || M_out > (int64_t)1 << 40) return NVFP4_ERR_ARG;
+  if (T >= (int64_t)0x7FFFFFFF || M_out >= (int64_t)0x7FFFFFFF) return NVFP4_ERR_UNSUPPORTED;
   if (in_dtype != NVFP4_BF16 && in_dtype != NVFP4_FP32) return NVFP4_ERR_ARG;
   if (G < 1) return NVFP4_ERR_ARG;
   if (G > NVFP4_GROUPS_MAX) return NVFP4_ERR_UNSUPPORTED;
@@ -145,7 +146,6 @@ int nvfp4_quantize_grouped(const void* x, int in_dtype, int64_t T, int64_t K,
   if (rw && (!q_row || !s_row)) return NVFP4_ERR_ARG;
   if (cw && (!q_col || !s_col)) return NVFP4_ERR_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_amax_init(row_amax, M_out, nullptr, 0, nullptr, noop, s)) return NVFP4_ERR_HIP;
   if (launch_grouped_amax(x, in_dtype, T, K, group_rows, G, align, M_out, row_amax, noop, s))
     return NVFP4_ERR_HIP;
   CastArgs a;

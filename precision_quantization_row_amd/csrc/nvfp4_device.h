@@ -199,4 +199,65 @@ __device__ __forceinline__ int64_t token_row(const GroupTable& gt, int G, int64_
   return r < gt.tok0[g + 1] - gt.tok0[g] ? gt.tok0[g] + r : -1;
 }
 
+// The same prefix sums held in the registers of one wave, 32-bit: lane l
+// keeps the inclusive ends of groups 4l .. 4l + 3 in token rows (tok) and in
+// padded rows (pad), saturating at 2^31 - 1; groups from G on end at
+// 0xFFFFFFFF. Built by every lane of a wave with no LDS and no barrier
+// (G <= 256). For rows below 2^31 - 1 the saturated ends lie past every row
+// looked up, so the map below is exact there.
+struct LaneEnds {
+  uint32_t tok[4], pad[4];
+};
+
+__device__ __forceinline__ LaneEnds lane_group_ends(const int64_t* rows, int G, int64_t align,
+                                                    int lane) {
+  constexpr uint32_t CL = 0x7FFFFFFFu;
+  LaneEnds e;
+  uint32_t st = 0u, sp = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int g = 4 * lane + k;
+    const int64_t n = g < G ? min(max(rows[g], (int64_t)0), (int64_t)CL) : 0;
+    st = min(st + (uint32_t)n, CL);
+    sp = min(sp + (uint32_t)min((n + align - 1) / align * align, (int64_t)CL), CL);
+    e.tok[k] = st;
+    e.pad[k] = sp;
+  }
+  // inclusive scan of the lane totals, then shift to an exclusive offset
+  uint32_t it = st, ip = sp;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t ot = (uint32_t)__shfl_up((int)it, off), op = (uint32_t)__shfl_up((int)ip, off);
+    if (lane >= off) {
+      it = min(it + ot, CL);
+      ip = min(ip + op, CL);
+    }
+  }
+  uint32_t xt = (uint32_t)__shfl_up((int)it, 1), xp = (uint32_t)__shfl_up((int)ip, 1);
+  if (lane == 0) xt = xp = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bool live = 4 * lane + k < G;
+    e.tok[k] = live ? min(e.tok[k] + xt, CL) : 0xFFFFFFFFu;
+    e.pad[k] = live ? min(e.pad[k] + xp, CL) : 0xFFFFFFFFu;
+  }
+  return e;
+}
+
+// Number of groups whose end (in `ends`) is at or before v: for a row v below
+// the last end, the index of the group holding it. v is wave-uniform; all 64
+// lanes active.
+__device__ __forceinline__ uint32_t groups_ending_by(const uint32_t (&ends)[4], uint32_t v) {
+  return __builtin_popcountll(__builtin_amdgcn_ballot_w64(ends[0] <= v)) +
+         __builtin_popcountll(__builtin_amdgcn_ballot_w64(ends[1] <= v)) +
+         __builtin_popcountll(__builtin_amdgcn_ballot_w64(ends[2] <= v)) +
+         __builtin_popcountll(__builtin_amdgcn_ballot_w64(ends[3] <= v));
+}
+
+// End of group g (wave-uniform, 0 <= g < 256) from the lane that holds it.
+__device__ __forceinline__ uint32_t group_end_at(const uint32_t (&ends)[4], uint32_t g) {
+  const uint32_t k = g & 3u;
+  const uint32_t v = k == 0u ? ends[0] : (k == 1u ? ends[1] : (k == 2u ? ends[2] : ends[3]));
+  return (uint32_t)__shfl((int)v, (int)(g >> 2));
+}
+
 }  // namespace nvfp4

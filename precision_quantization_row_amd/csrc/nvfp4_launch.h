@@ -21,8 +21,8 @@ int launch_tensor_amax(const void* x, int in_dtype, int64_t n, float* ta, const 
                        hipStream_t s);
 int launch_group_expand(float* ra, int64_t M, const int64_t* group_end, int64_t G,
                         const float* noop, hipStream_t s);
-// grouped tokens: group amax of each token group into the first padded row of
-// the group (ra zeroed beforehand), then expanded over the padded group
+// grouped tokens: the group amax of each token group over the group's padded
+// rows, 0 past the last group; every row of ra [M_out] is written
 int launch_grouped_amax(const void* x, int in_dtype, int64_t T, int64_t K, const int64_t* grows,
                         int64_t G, int64_t align, int64_t M_out, float* ra, const float* noop,
                         hipStream_t s);

@@ -107,6 +107,8 @@ def test_validation_rejects_before_launch():
                dict(sr=None), dict(qc=None)):
         assert g(**kw) == E, kw
     assert g(G=p.NVFP4_GROUPS_MAX + 1) == p.NVFP4_ERR_UNSUPPORTED
+    assert g(T=1 << 31) == p.NVFP4_ERR_UNSUPPORTED
+    assert g(M=(1 << 31) - 1) == p.NVFP4_ERR_UNSUPPORTED
     # group expansion
     assert lib.nvfp4_group_amax_expand(_fake(), 16, _fake(), 0, None, None) == E
     assert lib.nvfp4_group_amax_expand(None, 16, _fake(), 2, None, None) == E

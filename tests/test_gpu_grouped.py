@@ -153,6 +153,43 @@ def test_noop_leaves_every_buffer_untouched():
         assert (v == 0x3C).all(), k
 
 
+def _round64(n):
+    return -(-n // 64) * 64
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", ["mixed", "large_align", "short_x", "truncated", "many", "past"])
+def test_macro_tile_layouts(dtype, case):
+    """Layouts that take the macro-tile path (K a multiple of 256, M_out of 64):
+    16-row blocks that end a group mid-block, next to padding, empty groups,
+    token rows missing at the end of x, truncation, 256 groups, and rows past
+    the last group."""
+    K, align, T = 256, 16, None
+    if case == "mixed":
+        group_rows = [5, 0, 300, 17, 64, 1]
+    elif case == "large_align":
+        group_rows, align, K = [1000, 3, 250], 128, 512
+    elif case == "short_x":
+        group_rows, align, T = [200, 200], 32, 150
+    elif case == "truncated":
+        group_rows = [300, 300]
+    elif case == "many":
+        group_rows = np.random.RandomState(17).randint(0, 41, size=p.NVFP4_GROUPS_MAX).tolist()
+    else:
+        group_rows = [40, 90]
+    T = sum(group_rows) if T is None else T
+    x = _tokens(T, K, dtype, seed=len(case) + K)
+    m_out = _round64(_full_rows(group_rows, align))
+    if case == "truncated":
+        m_out = 512
+    if case == "past":
+        m_out += 256
+    _check(case, x, group_rows, align, m_out)
+    if case == "mixed" and dtype == torch.bfloat16:
+        _check("mixed rowwise", x, group_rows, align, m_out, colwise=False)
+        _check("mixed colwise", x, group_rows, align, m_out, rowwise=False)
+
+
 def test_transposed_copy_dequantizes_like_the_oracle():
     group_rows = [40, 0, 25]
     align = 32
