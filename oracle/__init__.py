@@ -56,6 +56,7 @@ def _load():
         "orc_quantize_rowwise": (None, [f32p, i64, i64, c_int, f32p, c_f, u8p, u8p]),
         "orc_quantize_colwise": (None, [f32p, i64, i64, c_int, f32p, c_f, u8p, u8p]),
         "orc_dequantize": (None, [u8p, u8p, i64, i64, c_int, f32p, c_f, f32p]),
+        "orc_quantize_2d": (None, [f32p, i64, i64, c_f, c_f, u8p, u8p, u8p, u8p]),
         "orc_amax_rows": (None, [f32p, i64, i64, f32p]),
         "orc_amax_cols": (None, [f32p, i64, i64, f32p]),
         "orc_amax_tensor": (c_f, [f32p, i64]),
@@ -201,6 +202,23 @@ def quantize_line(x, block_amax, bound: float = 448.0):
     _load().orc_quantize_line(_p(x, ctypes.c_float), n, 1, _p(ba, ctypes.c_float), float(bound),
                               _p(q, ctypes.c_uint8), _p(s, ctypes.c_uint8))
     return q, s
+
+
+def quantize_2d(X, amax: float, bound: float = 448.0):
+    """2-D 16x16 blocks under one per-tensor amax (a reading: the pages name
+    TE's 2-D weight blocks only through the switch that turns them off).
+    Returns (q_row, s_row, q_col, s_col) in the 1x16 layouts, each tile's
+    scale byte repeated on its 16 rows and 16 columns."""
+    X = _f32(X)
+    M, K = X.shape
+    q_row = np.zeros((M, (K + 1) // 2), dtype=np.uint8)
+    s_row = np.zeros((M, (K + 15) // 16), dtype=np.uint8)
+    q_col = np.zeros((K, (M + 1) // 2), dtype=np.uint8)
+    s_col = np.zeros((K, (M + 15) // 16), dtype=np.uint8)
+    _load().orc_quantize_2d(_p(X, ctypes.c_float), M, K, float(np.float32(amax)), float(bound),
+                            _p(q_row, ctypes.c_uint8), _p(s_row, ctypes.c_uint8),
+                            _p(q_col, ctypes.c_uint8), _p(s_col, ctypes.c_uint8))
+    return q_row, s_row, q_col, s_col
 
 
 def dequantize(q, s, R: int, C: int, mode: int, amax, bound: float = 448.0) -> np.ndarray:

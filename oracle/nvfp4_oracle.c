@@ -151,17 +151,11 @@ float orc_global_encode_scale(float a, float bound) {
  * Op order of s32 / enc is a reading; D is the pages' decode expression, so
  * quantize and dequantize share one FP32 decode scale per block.
  * ------------------------------------------------------------------------- */
-static void quantize_block(const float *x, int64_t stride, int n, float a,
-                           float bound, uint8_t *codes, uint8_t *scale_byte) {
+/* The scale byte and the encode factor of a block whose max magnitude is
+ * bamax, under second-level amax a (the steps s32 .. enc above). */
+static float block_scale(float bamax, float a, float bound, uint8_t *scale_byte) {
   const float s_enc = orc_global_encode_scale(a, bound);
   const float f_inv = orc_factor_inv(bound);
-  float bamax = 0.0f;
-  for (int k = 0; k < n; ++k) {
-    float v = x[(int64_t)k * stride];
-    assert(isfinite(v));
-    float m = fabsf(v);
-    if (m > bamax) bamax = m;
-  }
   float s32 = (bamax / 6.0f) * s_enc;
   if (s32 > 448.0f) s32 = 448.0f;
   uint8_t b = orc_e4m3_encode(s32);
@@ -172,8 +166,21 @@ static void quantize_block(const float *x, int64_t stride, int n, float a,
     enc = 1.0f / d;
     if (enc > FLT_MAX) enc = FLT_MAX;
   }
-  for (int k = 0; k < n; ++k) codes[k] = orc_e2m1_encode(x[(int64_t)k * stride] * enc);
   *scale_byte = b;
+  return enc;
+}
+
+static void quantize_block(const float *x, int64_t stride, int n, float a,
+                           float bound, uint8_t *codes, uint8_t *scale_byte) {
+  float bamax = 0.0f;
+  for (int k = 0; k < n; ++k) {
+    float v = x[(int64_t)k * stride];
+    assert(isfinite(v));
+    float m = fabsf(v);
+    if (m > bamax) bamax = m;
+  }
+  const float enc = block_scale(bamax, a, bound, scale_byte);
+  for (int k = 0; k < n; ++k) codes[k] = orc_e2m1_encode(x[(int64_t)k * stride] * enc);
 }
 
 /* Quantize one line of n elements (element k at x[k*stride]).
@@ -237,6 +244,49 @@ void orc_quantize_colwise(const float *X, int64_t M, int64_t K, int mode,
     for (int64_t b = 0; b < sb; ++b) ba[b] = block_amax_of(mode, amax, j, b);
     orc_quantize_line(X + j, M, K, ba, bound, q + j * qb, s + j * sb);
     free(ba);
+  }
+}
+
+/* ---------------------------------------------------------------------------
+ * 2-D blocks ([P4] description: the 1x16 weight option mirrors TE's switch
+ * that turns 2-D quantization off, so TE's default weight blocks are 2-D; the
+ * pages name the option and define nothing more). Reading: a block is a 16 x 16
+ * tile of X (rows 16I .., columns 16J .., cut at the matrix edge), its max
+ * magnitude gives one scale through the same steps as a 1x16 block, under one
+ * per-tensor amax a, and every element of the tile is encoded with that
+ * scale. Both copies keep the 1x16 layouts: row r holds the scale of tile
+ * (r/16, J) at s_row[r][J], column c the scale of tile (I, c/16) at
+ * s_col[c][I], so a tile's byte appears on each of its 16 rows and 16
+ * columns, and q_col is the exact transpose of q_row.
+ * ------------------------------------------------------------------------- */
+void orc_quantize_2d(const float *X, int64_t M, int64_t K, float a, float bound,
+                     uint8_t *q_row, uint8_t *s_row, uint8_t *q_col, uint8_t *s_col) {
+  const int64_t qrb = (K + 1) / 2, srb = (K + 15) / 16;
+  const int64_t qcb = (M + 1) / 2, scb = (M + 15) / 16;
+  memset(q_row, 0, (size_t)(M * qrb));
+  memset(q_col, 0, (size_t)(K * qcb));
+  for (int64_t ti = 0; ti < scb; ++ti) {
+    for (int64_t tj = 0; tj < srb; ++tj) {
+      const int64_t r0 = 16 * ti, r1 = r0 + 16 < M ? r0 + 16 : M;
+      const int64_t c0 = 16 * tj, c1 = c0 + 16 < K ? c0 + 16 : K;
+      float tamax = 0.0f;
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c = c0; c < c1; ++c) {
+          assert(isfinite(X[r * K + c]));
+          float m = fabsf(X[r * K + c]);
+          if (m > tamax) tamax = m;
+        }
+      uint8_t b;
+      const float enc = block_scale(tamax, a, bound, &b);
+      for (int64_t r = r0; r < r1; ++r) s_row[r * srb + tj] = b;
+      for (int64_t c = c0; c < c1; ++c) s_col[c * scb + ti] = b;
+      for (int64_t r = r0; r < r1; ++r)
+        for (int64_t c = c0; c < c1; ++c) {
+          const uint8_t code = orc_e2m1_encode(X[r * K + c] * enc);
+          q_row[r * qrb + c / 2] |= (uint8_t)((c & 1) ? code << 4 : code);
+          q_col[c * qcb + r / 2] |= (uint8_t)((r & 1) ? code << 4 : code);
+        }
+    }
   }
 }
 
