@@ -86,6 +86,16 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
     ft = lambda i: p.nvfp4_amax_rowcol(xs[i & 1], None, None, tensor_amax=ta)
     ft(0)
     res["tensor_amax_bf16_8192x28672"] = _row(timed(ft, n) * 1e3, xb + 4, "X read once")
+    # 2-D 16 x 16 tile scales, both copies, on the same matrix (per-tensor amax
+    # already in ta)
+    out = p.empty_outputs(M, K, dev)
+    f2d = lambda i: p.nvfp4_quantize_2d(xs[i & 1], ta, bound, out["q_row"], out["s_row"],
+                                        out["q_col"], out["s_col"])
+    f2d(0)
+    cb2 = xb + 4 + 2 * (M * (K // 2) + M * (K // 16))
+    res["quantize_2d_bf16_8192x28672"] = _row(timed(f2d, n) * 1e3, cb2,
+                                              "X read once, both copies written")
+    del out
 
     w = workloads.make("fp32_edge")
     M, K = w.shape

@@ -130,6 +130,23 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
                              float bound, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
                              uint8_t* s_col, const float* noop, void* stream);
 
+/* 2-D 16 x 16 blocks (backward-overrides PR description: its 1x16 weight
+ * option mirrors TE's switch that turns 2-D weight quantization off, so 2-D
+ * blocks are TE's default for weights; the pages define nothing more). One
+ * scale per 16 x 16 tile of X, from the tile's max magnitude through the
+ * same steps as a 1x16 block, under the per-tensor amax tensor_amax[0]
+ * (device float, e.g. from nvfp4_amax_rowcol). Tiles at the matrix edge use
+ * the elements that exist. The outputs keep the 1x16 layouts of
+ * nvfp4_quantize_transpose: each tile's scale byte is written on its 16 rows
+ * (s_row) and its 16 columns (s_col), and q_col is the exact transpose of
+ * q_row, so nvfp4_dequantize in mode TENSOR decodes either copy.
+ *   q_row [M][ceil(K/2)] and s_row [M][ceil(K/16)] (both or neither)
+ *   q_col [K][ceil(M/2)] and s_col [K][ceil(M/16)] (both or neither)
+ * At least one copy must be requested. */
+int nvfp4_quantize_2d(const void* x, int in_dtype, int64_t M, int64_t K, const float* tensor_amax,
+                      float bound, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                      const float* noop, void* stream);
+
 /* Grouped tokens, padded on the way in, in one call (grouped-GEMM PR
  * description: ragged token groups zero-padded to an alignment before
  * quantization, per-group global scales from each group's amax expanded to

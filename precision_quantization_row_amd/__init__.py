@@ -39,7 +39,8 @@ NVFP4_FLAG_FORCE_TWO_KERNEL = 1
 
 # Every entry point include/nvfp4.h declares.
 EXPORTED = ("nvfp4_amax_path", "nvfp4_amax_rowcol", "nvfp4_group_amax_expand",
-            "nvfp4_quantize_transpose", "nvfp4_quantize_grouped", "nvfp4_dequantize",
+            "nvfp4_quantize_transpose", "nvfp4_quantize_2d", "nvfp4_quantize_grouped",
+            "nvfp4_dequantize",
             "nvfp4_status_string")
 
 NVFP4_GROUPS_MAX = 256
@@ -76,6 +77,8 @@ def load_library():
     lib.nvfp4_quantize_transpose.restype = c_int
     lib.nvfp4_quantize_transpose.argtypes = [vp, c_int, i64, i64, c_int, f32p, c_int, f32p, c_f,
                                              u8p, u8p, u8p, u8p, f32p, vp]
+    lib.nvfp4_quantize_2d.restype = c_int
+    lib.nvfp4_quantize_2d.argtypes = [vp, c_int, i64, i64, f32p, c_f, u8p, u8p, u8p, u8p, f32p, vp]
     lib.nvfp4_quantize_grouped.restype = c_int
     lib.nvfp4_quantize_grouped.argtypes = [vp, c_int, i64, i64, i64p, i64, i64, i64, c_f, f32p,
                                            u8p, u8p, u8p, u8p, f32p, vp]
@@ -208,6 +211,31 @@ def nvfp4_quantize_transpose(x: torch.Tensor, row_mode: int, row_amax: Optional[
                                       _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col),
                                       _ptr(noop), _stream(stream, dev))
     _check("nvfp4_quantize_transpose", st)
+
+
+def nvfp4_quantize_2d(x: torch.Tensor, tensor_amax: torch.Tensor, bound: float,
+                      q_row: Optional[torch.Tensor], s_row: Optional[torch.Tensor],
+                      q_col: Optional[torch.Tensor], s_col: Optional[torch.Tensor],
+                      noop: Optional[torch.Tensor] = None, stream=None) -> None:
+    """x [M, K] with 16 x 16 tile scales under the per-tensor amax tensor_amax [1]."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    _dev(x, "x", (torch.bfloat16, torch.float32))
+    M, K = x.shape
+    dev = x.device
+    _dev(tensor_amax, "tensor_amax", _F32, 1, dev)
+    if q_row is not None:
+        _dev(q_row, "q_row", (torch.uint8,), M * ((K + 1) // 2), dev)
+        _dev(s_row, "s_row", _SCALE_DTYPES, M * ((K + 15) // 16), dev)
+    if q_col is not None:
+        _dev(q_col, "q_col", (torch.uint8,), K * ((M + 1) // 2), dev)
+        _dev(s_col, "s_col", _SCALE_DTYPES, K * ((M + 15) // 16), dev)
+    _dev(noop, "noop", _F32, 1, dev)
+    st = lib.nvfp4_quantize_2d(_ptr(x), _dtype_code(x), M, K, _ptr(tensor_amax),
+                               ctypes.c_float(bound), _ptr(q_row), _ptr(s_row), _ptr(q_col),
+                               _ptr(s_col), _ptr(noop), _stream(stream, dev))
+    _check("nvfp4_quantize_2d", st)
 
 
 def padded_rows_max(T: int, G: int, align: int) -> int:

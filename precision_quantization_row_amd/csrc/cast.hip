@@ -63,6 +63,8 @@ struct CastK {
   // token row token_row(r) of x, or is a zero row (padding, past the groups)
   const int64_t* grp_rows;
   int64_t grp_G, grp_align, grp_T;
+  // 2-D blocks: one scale per 16 x 16 tile, per-tensor amax row_amax[0]
+  int blk2d;
 };
 
 // Lane block storage: NW dwords per row. BF16: 4 dwords = 8 values (element
@@ -436,6 +438,70 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
   }
 }
 
+// 2-D blocks: the lane pair (l, l ^ 1) holds one 16 x 16 tile (16 rows, 8
+// columns each). The tile's max magnitude gives one scale (per-tensor amax a,
+// S_enc s_enc) for all its 16 rows and 16 columns, so every element is
+// multiplied once and both copies encode the same products: the rowwise codes
+// pair neighbouring columns, the transposed codes neighbouring rows.
+template <typename T, bool ROWW, bool COLW, class Store, class Mid>
+__device__ __forceinline__ void process_block_2d(const uint32_t (&w)[16][Blk<T>::NW],
+                                                 const Store& st, float a, float s_enc,
+                                                 float f_inv, const Mid& mid) {
+  constexpr int NW = Blk<T>::NW;
+  uint32_t m = 0u;
+  if constexpr (sizeof(T) == 2) {
+    uint32_t cm[NW];
+#pragma unroll
+    for (int d = 0; d < NW; ++d) cm[d] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int d = 0; d < NW; ++d) cm[d] = pk_max_u16(cm[d], w[i][d] & kAbsBf16x2);
+    const uint32_t t = pk_max_u16(pk_max_u16(cm[0], cm[1]), pk_max_u16(cm[2], cm[3]));
+    m = max(t & 0xFFFFu, t >> 16) << 16;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int k = 0; k < NW; ++k) m = max(m, w[i][k] & kAbsF32);
+  }
+  m = max(m, dpp_swap1(m));
+  mid();
+  uint32_t byte;
+  float enc;
+  if (!block_scale_fast(__uint_as_float(m), a, s_enc, f_inv, &byte, &enc))
+    block_scale(__uint_as_float(m), a, s_enc, f_inv, &byte, &enc);
+  if constexpr (ROWW) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.row_scale(j, byte);
+  }
+  uint32_t cc[8][2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float pv[2][8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pv[e][k] = elem<T>(w, 2 * j + e, k) * enc;
+    if constexpr (ROWW) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        st.row_codes(2 * j + e, e2m1_pack8(pv[e][0], pv[e][1], pv[e][2], pv[e][3], pv[e][4],
+                                           pv[e][5], pv[e][6], pv[e][7]));
+    }
+    if constexpr (COLW) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        cc[k][j >> 2] = cvt_fp4x2_sel((j & 3) ? cc[k][j >> 2] : __float_as_uint(pv[0][k]), pv[0][k],
+                                      pv[1][k], j);
+    }
+  }
+  if constexpr (COLW) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) st.col(k, cc[k][0], cc[k][1], byte);
+  }
+}
+
 // Row / column tables in LDS (a pointer and a base index).
 struct LdsTab {
   const float* pa;
@@ -545,6 +611,10 @@ struct StoreIT {
   __device__ __forceinline__ void col_scale(int k, uint32_t byte) const {
     sc[(32 * k + L) * 16 + slot] = (uint8_t)byte;
   }
+  __device__ __forceinline__ void col(int k, uint32_t w0, uint32_t w1, uint32_t byte) const {
+    col_codes(k, w0, w1);
+    col_scale(k, byte);
+  }
 };
 
 // Grouped tokens in the interior kernel. The group table is built once per
@@ -627,9 +697,11 @@ __device__ __forceinline__ WaveRows grouped_wave_rows(const ITSmem& sm, int G, u
   return w;
 }
 
-template <typename T, bool ROWW, bool COLW, bool GRP>
+// VAR: 0 = 1x16 blocks, 1 = grouped tokens (1x16), 2 = 2-D 16 x 16 blocks
+template <typename T, bool ROWW, bool COLW, int VAR>
 __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_kernel(const CastK p) {
   if (p.noop != nullptr && *p.noop == 1.0f) return;
+  constexpr bool GRP = VAR == 1, B2D = VAR == 2;
   constexpr int NW = Blk<T>::NW;
   __shared__ __attribute__((aligned(16))) ITSmem sm;
   const T* __restrict__ x = static_cast<const T*>(p.x);
@@ -652,6 +724,12 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
   const uint32_t rowbytes = (uint32_t)(K * (int64_t)sizeof(T));
   const int64_t qrs = (K + 1) / 2, srs = (K + 15) / 16;
   const int64_t qcs = (p.M + 1) / 2, scs = (p.M + 15) / 16;
+  // 2-D blocks: the per-tensor amax and its S_enc
+  float a2d = 0.0f, s2d = 1.0f;
+  if constexpr (B2D) {
+    a2d = ROWW ? p.row_amax[0] : p.col_amax[0];
+    s2d = global_encode_scale(a2d, p.F);
+  }
 
   // sub-step v: macro tile origin (m0, c0); false when outside the interior
   // (uniform per workgroup, the same for both sub-steps of a tile)
@@ -725,7 +803,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     // when the strip changes), or the group amax of the lane's 16-row block
     // (mode 2)
     ColLds ctab{&sm.ca[8 * L], &sm.cs[8 * L]};
-    if constexpr (COLW) {
+    if constexpr (COLW && !B2D) {
       if (GRP || p.col_mode == 2) {
         if (L < 8) {
           const float a = p.col_amax[rs + 32 * wv + 16 * h];
@@ -744,7 +822,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
       }
     }
     // row amax / S_enc of the wave's 32 rows
-    if constexpr (ROWW) {
+    if constexpr (ROWW && !B2D) {
       if (lane < 32) {
         const float a = (p.row_mode == 0) ? p.row_amax[0] : p.row_amax[rs + 32 * wv + lane];
         sm.ra[wv][lane] = a;
@@ -805,8 +883,11 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
         if (vn < n_v) prefetch(m0n + (vn & 1) * IT_SUB, c0n, WaveRows{0, 0u, 0u, 0u, 0u});
       }
     };
-    process_block_batched<T, ROWW, COLW>(w, st, h, par, LdsTab{sm.ra[wv], sm.rs[wv], 0}, ctab,
-                                         p.F_inv, mid);
+    if constexpr (B2D)
+      process_block_2d<T, ROWW, COLW>(w, st, a2d, s2d, p.F_inv, mid);
+    else
+      process_block_batched<T, ROWW, COLW>(w, st, h, par, LdsTab{sm.ra[wv], sm.rs[wv], 0}, ctab,
+                                           p.F_inv, mid);
     __syncthreads();  // the sub-step's staged outputs are complete
 
     if constexpr (ROWW) {  // 128 rows x 16 B
@@ -861,7 +942,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
 // workgroup per segment of rows_per_wg rows of one strip, checked loads and
 // stores. Launched over a rectangle: segment seg0 + b / nstrips of the row
 // range [rstart, rend), strip strip0 + b % nstrips.
-template <typename T, bool ROWW, bool COLW>
+template <typename T, bool ROWW, bool COLW, bool B2D>
 __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   constexpr int NW = Blk<T>::NW;
@@ -887,7 +968,7 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
   const int64_t rs = p.rstart + seg * p.rows_per_wg;
   const int64_t re = min(rs + p.rows_per_wg, p.rend);
 
-  if constexpr (ROWW) {
+  if constexpr (ROWW && !B2D) {
     for (int i = tid; i < (int)p.rows_per_wg; i += 256) {
       float a = 0.0f;
       if (rs + i < re) a = (p.row_mode == 0) ? p.row_amax[0] : p.row_amax[rs + i];
@@ -940,6 +1021,11 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
       }
     }
     st.rb0 = rb0;
+    if constexpr (B2D) {
+      const float a = ROWW ? p.row_amax[0] : p.col_amax[0];
+      process_block_2d<T, ROWW, COLW>(w, st, a, global_encode_scale(a, p.F), p.F_inv, NoMid());
+      continue;
+    }
     if constexpr (COLW) {
       if (p.col_mode == 2) {
         const float ga = rb0 < re ? p.col_amax[rb0] : 0.0f;
@@ -956,7 +1042,7 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
   }
 }
 
-template <typename T, bool ROWW, bool COLW, bool GRP>
+template <typename T, bool ROWW, bool COLW, int VAR>
 static int interior_grid() {
   // resident interior workgroups on the device (a multiple of 8), per device
   static int cache[64] = {0};
@@ -965,7 +1051,7 @@ static int interior_grid() {
   if (cache[dev] == 0) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW, GRP>), 256, 0) !=
+            &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW, VAR>), 256, 0) !=
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
@@ -982,13 +1068,17 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
     // all resident workgroups: a partly idle last round costs less than
     // fewer waves per CU
     if (k.grp_G > 0) {
-      const int64_t G = interior_grid<T, ROWW, COLW, true>();
-      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, true>), dim3((unsigned)G), dim3(256),
-                         0, s, k);
+      const int64_t G = interior_grid<T, ROWW, COLW, 1>();
+      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 1>), dim3((unsigned)G), dim3(256), 0,
+                         s, k);
+    } else if (k.blk2d) {
+      const int64_t G = interior_grid<T, ROWW, COLW, 2>();
+      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 2>), dim3((unsigned)G), dim3(256), 0,
+                         s, k);
     } else {
-      const int64_t G = interior_grid<T, ROWW, COLW, false>();
-      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, false>), dim3((unsigned)G), dim3(256),
-                         0, s, k);
+      const int64_t G = interior_grid<T, ROWW, COLW, 0>();
+      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 0>), dim3((unsigned)G), dim3(256), 0,
+                         s, k);
     }
   }
   // edge rectangles: (1) the partial last strip over all rows,
@@ -1009,8 +1099,12 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
     k.seg0 = 0;
     k.strip0 = strip0;
     k.nstrips = nstrips;
-    hipLaunchKernelGGL((cast_edge_kernel<T, ROWW, COLW>), dim3((unsigned)(segs * nstrips)), block,
-                       0, s, k);
+    if (k.blk2d)
+      hipLaunchKernelGGL((cast_edge_kernel<T, ROWW, COLW, true>), dim3((unsigned)(segs * nstrips)),
+                         block, 0, s, k);
+    else
+      hipLaunchKernelGGL((cast_edge_kernel<T, ROWW, COLW, false>), dim3((unsigned)(segs * nstrips)),
+                         block, 0, s, k);
   };
   const int64_t strips = (a.K + CAST_STRIP_COLS - 1) / CAST_STRIP_COLS;
   if (ntiles > 0)  // the interior spans every column: the rows below it remain
@@ -1040,6 +1134,7 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
   k.grp_G = a.grp_G;
   k.grp_align = a.grp_align;
   k.grp_T = a.grp_T;
+  k.blk2d = a.blk2d;
   constexpr int V = 16 / sizeof(T);
   k.vec_load = ((a.K % V) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
   k.row_store4 = (a.K % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0);

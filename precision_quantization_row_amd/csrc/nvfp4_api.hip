@@ -127,6 +127,38 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
   return launch_cast(a, static_cast<hipStream_t>(stream)) ? NVFP4_ERR_HIP : NVFP4_OK;
 }
 
+int nvfp4_quantize_2d(const void* x, int in_dtype, int64_t M, int64_t K, const float* tensor_amax,
+                      float bound, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                      const float* noop, void* stream) {
+  if (x == nullptr || tensor_amax == nullptr || M < 1 || K < 1) return NVFP4_ERR_ARG;
+  if (M > (int64_t)1 << 40 || K > (int64_t)1 << 40) return NVFP4_ERR_ARG;
+  if (in_dtype != NVFP4_BF16 && in_dtype != NVFP4_FP32) return NVFP4_ERR_ARG;
+  if (!valid_bound(bound)) return NVFP4_ERR_ARG;
+  const bool rw = q_row != nullptr || s_row != nullptr;
+  const bool cw = q_col != nullptr || s_col != nullptr;
+  if (!rw && !cw) return NVFP4_ERR_ARG;
+  if (rw && (!q_row || !s_row)) return NVFP4_ERR_ARG;
+  if (cw && (!q_col || !s_col)) return NVFP4_ERR_ARG;
+  CastArgs a;
+  a.x = x;
+  a.in_dtype = in_dtype;
+  a.M = M;
+  a.K = K;
+  a.row_mode = NVFP4_AMAX_TENSOR;
+  a.row_amax = tensor_amax;
+  a.col_mode = NVFP4_AMAX_TENSOR;
+  a.col_amax = tensor_amax;
+  a.F = bound * 6.0f;
+  a.F_inv = 1.0f / a.F;
+  a.q_row = rw ? q_row : nullptr;
+  a.s_row = rw ? s_row : nullptr;
+  a.q_col = cw ? q_col : nullptr;
+  a.s_col = cw ? s_col : nullptr;
+  a.noop = noop;
+  a.blk2d = 1;
+  return launch_cast(a, static_cast<hipStream_t>(stream)) ? NVFP4_ERR_HIP : NVFP4_OK;
+}
+
 int nvfp4_quantize_grouped(const void* x, int in_dtype, int64_t T, int64_t K,
                            const int64_t* group_rows, int64_t G, int64_t align, int64_t M_out,
                            float bound, float* row_amax, uint8_t* q_row, uint8_t* s_row,

@@ -42,6 +42,8 @@ struct CastArgs {
   // token row token_row(r) or a zero row (padding)
   const int64_t* grp_rows = nullptr;
   int64_t grp_G = 0, grp_align = 16, grp_T = 0;
+  // 2-D 16 x 16 blocks (row and column mode TENSOR, one amax)
+  int blk2d = 0;
 };
 int launch_cast(const CastArgs& a, hipStream_t s);
 

@@ -97,6 +97,12 @@ def test_validation_rejects_before_launch():
     assert d(bound=500.0) == E
     assert d(R=0) == E
     assert d(C=0) == E
+    # 2-D blocks: missing amax / buffers, sizes, bound, dtype
+    t = lambda M=32, K=32, ta=_fake(), bound=448.0, qr=_fake(), sr=_fake(), qc=_fake(), sc=_fake(), \
+        dt=0, x=_fake(): lib.nvfp4_quantize_2d(x, dt, M, K, ta, f(bound), qr, sr, qc, sc, None, None)
+    for kw in (dict(M=0), dict(K=0), dict(ta=None), dict(x=None), dict(bound=0.0), dict(bound=449.0),
+               dict(dt=2), dict(qr=None, sr=None, qc=None, sc=None), dict(sr=None), dict(sc=None)):
+        assert t(**kw) == E, kw
     # grouped tokens: sizes, group count, alignment, bound, missing buffers
     g = lambda T=64, K=32, G=4, align=16, M=128, bound=448.0, x=_fake(), gr=_fake(), ra=_fake(), \
         qr=_fake(), sr=_fake(), qc=_fake(), sc=_fake(), dt=0: lib.nvfp4_quantize_grouped(
