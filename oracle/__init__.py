@@ -234,6 +234,18 @@ def dequantize(q, s, R: int, C: int, mode: int, amax, bound: float = 448.0) -> n
     return y
 
 
+def quantize_dequantize(X, mode: int, amax, bound: float = 448.0):
+    """Backward-overrides PR description, "dequantized" policy: the rowwise
+    fprop codes and scales are kept and the backward GEMMs run in BF16 on
+    their dequantization. This is the rowwise quantize followed by the
+    dequantize of that copy, nothing else (both steps pinned on their own).
+    Returns (q [M][ceil(K/2)], s [M][ceil(K/16)], y FP32 [M][K])."""
+    X = _f32(X)
+    M, K = X.shape
+    q, s = quantize_rowwise(X, mode, amax, bound)
+    return q, s, dequantize(q, s, M, K, mode, amax, bound)
+
+
 def to_bf16_bits(y: np.ndarray) -> np.ndarray:
     """Round-to-nearest-even FP32 -> BF16 (as uint16 bit patterns), by torch's
     conversion (a library routine standing in for the rounding step)."""

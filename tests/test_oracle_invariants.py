@@ -229,3 +229,16 @@ def test_ragged_padded_equals_aligned_construction():
             qs, ss = oracle.quantize_rowwise(xs, oracle.MODE_TENSOR, [ta], 448.0)
             assert np.array_equal(q[start:start + n], qs) and np.array_equal(s[start:start + n], ss)
         start = end
+
+
+# -------------------------------------------------- quantize, then dequantize
+@pytest.mark.parametrize("mode", [oracle.MODE_TENSOR, oracle.MODE_LINE])
+def test_quantize_dequantize_is_the_composition(mode):
+    """The fused form has no arithmetic of its own: rowwise codes, then their
+    dequantization (whose error bound the test above pins)."""
+    x = _f32(workloads.make("tiny_rowscale", (48, 80)).x)
+    a = [oracle.amax_tensor(x)] if mode == oracle.MODE_TENSOR else oracle.amax_rows(x)
+    q, s, y = oracle.quantize_dequantize(x, mode, a, 256.0)
+    q2, s2 = oracle.quantize_rowwise(x, mode, a, 256.0)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    assert np.array_equal(y, oracle.dequantize(q2, s2, 48, 80, mode, a, 256.0))
