@@ -96,6 +96,17 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
     res["quantize_2d_bf16_8192x28672"] = _row(timed(f2d, n) * 1e3, cb2,
                                               "X read once, both copies written")
     del out
+    # rowwise codes and their BF16 dequantization in one pass (row amax given)
+    p.nvfp4_amax_rowcol(xs[0], ra)
+    qr = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
+    sr = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
+    yq = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
+    fq = lambda i: p.nvfp4_quantize_dequantize(xs[i & 1], p.NVFP4_AMAX_LINE, ra, bound, yq, qr, sr)
+    fq(0)
+    res["quantize_dequantize_bf16_8192x28672"] = _row(
+        timed(fq, n) * 1e3, xb + 4 * M + M * (K // 2) + M * (K // 16) + M * K * 2,
+        "X read once, rowwise codes + scales and the BF16 operand written")
+    del qr, sr, yq
 
     w = workloads.make("fp32_edge")
     M, K = w.shape

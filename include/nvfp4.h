@@ -195,6 +195,20 @@ int nvfp4_dequantize(const uint8_t* q, const uint8_t* sc, int64_t R, int64_t C, 
                      const float* amax, float bound, void* y, int out_dtype, const float* noop,
                      void* stream);
 
+/* Rowwise quantize and the dequantize of that copy in one pass over X
+ * (backward-overrides PR description: the "dequantized" policy keeps the
+ * rowwise fprop codes and scales and runs the backward GEMMs in BF16 on their
+ * dequantization). Equal to nvfp4_quantize_transpose (rowwise copy only)
+ * followed by nvfp4_dequantize of that copy, with X read once.
+ *   row_mode / row_amax: TENSOR ([1]) or LINE ([M])
+ *   q_row [M][ceil(K/2)], s_row [M][ceil(K/16)]: both or neither (NULL:
+ *          only the dequantized operand is written)
+ *   y [M][K], out_dtype BF16 (round to nearest even of the FP32 value) or
+ *          FP32 */
+int nvfp4_quantize_dequantize(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
+                              const float* row_amax, float bound, uint8_t* q_row, uint8_t* s_row,
+                              void* y, int out_dtype, const float* noop, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* nvfp4_status_string(int status);
 

@@ -40,7 +40,7 @@ NVFP4_FLAG_FORCE_TWO_KERNEL = 1
 # Every entry point include/nvfp4.h declares.
 EXPORTED = ("nvfp4_amax_path", "nvfp4_amax_rowcol", "nvfp4_group_amax_expand",
             "nvfp4_quantize_transpose", "nvfp4_quantize_2d", "nvfp4_quantize_grouped",
-            "nvfp4_dequantize",
+            "nvfp4_quantize_dequantize", "nvfp4_dequantize",
             "nvfp4_status_string")
 
 NVFP4_GROUPS_MAX = 256
@@ -82,6 +82,9 @@ def load_library():
     lib.nvfp4_quantize_grouped.restype = c_int
     lib.nvfp4_quantize_grouped.argtypes = [vp, c_int, i64, i64, i64p, i64, i64, i64, c_f, f32p,
                                            u8p, u8p, u8p, u8p, f32p, vp]
+    lib.nvfp4_quantize_dequantize.restype = c_int
+    lib.nvfp4_quantize_dequantize.argtypes = [vp, c_int, i64, i64, c_int, f32p, c_f, u8p, u8p, vp,
+                                              c_int, f32p, vp]
     lib.nvfp4_dequantize.restype = c_int
     lib.nvfp4_dequantize.argtypes = [u8p, u8p, i64, i64, c_int, f32p, c_f, vp, c_int, f32p, vp]
     _lib = lib
@@ -271,6 +274,30 @@ def nvfp4_quantize_grouped(x: torch.Tensor, group_rows: torch.Tensor, align: int
                                     _ptr(s_row), _ptr(q_col), _ptr(s_col), _ptr(noop),
                                     _stream(stream, dev))
     _check("nvfp4_quantize_grouped", st)
+
+
+def nvfp4_quantize_dequantize(x: torch.Tensor, row_mode: int, row_amax: torch.Tensor,
+                              bound: float, y: torch.Tensor, q_row: Optional[torch.Tensor] = None,
+                              s_row: Optional[torch.Tensor] = None,
+                              noop: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Rowwise codes of x [M, K] (optional) and their dequantization y [M, K]
+    (bfloat16 or float32) in one pass."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    _dev(x, "x", (torch.bfloat16, torch.float32))
+    M, K = x.shape
+    dev = x.device
+    _dev(row_amax, "row_amax", _F32, _amax_numel(row_mode, M, K), dev)
+    _dev(y, "y", (torch.bfloat16, torch.float32), M * K, dev)
+    if q_row is not None:
+        _dev(q_row, "q_row", (torch.uint8,), M * ((K + 1) // 2), dev)
+        _dev(s_row, "s_row", _SCALE_DTYPES, M * ((K + 15) // 16), dev)
+    _dev(noop, "noop", _F32, 1, dev)
+    st = lib.nvfp4_quantize_dequantize(_ptr(x), _dtype_code(x), M, K, row_mode, _ptr(row_amax),
+                                       ctypes.c_float(bound), _ptr(q_row), _ptr(s_row), _ptr(y),
+                                       _dtype_code(y), _ptr(noop), _stream(stream, dev))
+    _check("nvfp4_quantize_dequantize", st)
 
 
 def nvfp4_dequantize(q: torch.Tensor, sc: torch.Tensor, R: int, C: int, amax_mode: int,

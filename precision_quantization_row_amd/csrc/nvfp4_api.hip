@@ -203,6 +203,33 @@ int nvfp4_quantize_grouped(const void* x, int in_dtype, int64_t T, int64_t K,
   return launch_cast(a, s) ? NVFP4_ERR_HIP : NVFP4_OK;
 }
 
+int nvfp4_quantize_dequantize(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
+                              const float* row_amax, float bound, uint8_t* q_row, uint8_t* s_row,
+                              void* y, int out_dtype, const float* noop, void* stream) {
+  if (x == nullptr || row_amax == nullptr || y == nullptr || M < 1 || K < 1) return NVFP4_ERR_ARG;
+  if (M > (int64_t)1 << 40 || K > (int64_t)1 << 40) return NVFP4_ERR_ARG;
+  if (in_dtype != NVFP4_BF16 && in_dtype != NVFP4_FP32) return NVFP4_ERR_ARG;
+  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_FP32) return NVFP4_ERR_ARG;
+  if (row_mode != NVFP4_AMAX_TENSOR && row_mode != NVFP4_AMAX_LINE) return NVFP4_ERR_ARG;
+  if (!valid_bound(bound)) return NVFP4_ERR_ARG;
+  if ((q_row == nullptr) != (s_row == nullptr)) return NVFP4_ERR_ARG;
+  QdqArgs a;
+  a.x = x;
+  a.in_dtype = in_dtype;
+  a.M = M;
+  a.K = K;
+  a.amax_mode = row_mode;
+  a.amax = row_amax;
+  a.F = bound * 6.0f;
+  a.F_inv = 1.0f / a.F;
+  a.q = q_row;
+  a.sc = s_row;
+  a.y = y;
+  a.out_dtype = out_dtype;
+  a.noop = noop;
+  return launch_qdq(a, static_cast<hipStream_t>(stream)) ? NVFP4_ERR_HIP : NVFP4_OK;
+}
+
 int nvfp4_dequantize(const uint8_t* q, const uint8_t* sc, int64_t R, int64_t C, int amax_mode,
                      const float* amax, float bound, void* y, int out_dtype, const float* noop,
                      void* stream) {

@@ -119,6 +119,19 @@ __device__ __forceinline__ bool block_scale_fast(float bamax, float a, float s_e
   return (bb >= 0x01000000u) & ((db - 0x00800000u) < 0x7E000000u);
 }
 
+// block_scale that also returns the block's decode scale D (the factor the
+// dequantize multiplies each code value by).
+__device__ __forceinline__ void block_scale_dec(float bamax, float a, float s_enc, float f_inv,
+                                                uint32_t* byte, float* enc, float* dec) {
+  const float s32 = fminf(div6_rn(bamax) * s_enc, kE4M3Max);
+  const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(s32, s32, 0, false);
+  *byte = (uint32_t)pk & 0xFFu;
+  const float sq = __builtin_amdgcn_cvt_f32_fp8(pk, 0);
+  const float d = (sq * a) * f_inv;
+  *dec = d;
+  *enc = (d == 0.0f) ? 0.0f : recip_rn(d);
+}
+
 // --------------------------------------------------------------- E2M1 encode
 // v_cvt_scalef32_pk_fp4_f32 with scale 1.0 converts two fp32 values to E2M1
 // with round-to-nearest-even, saturation at 6 and the sign bit kept (-0 and

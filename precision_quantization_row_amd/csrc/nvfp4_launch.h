@@ -60,4 +60,19 @@ struct DequantArgs {
 };
 int launch_dequant(const DequantArgs& a, hipStream_t s);
 
+// rowwise quantize and the dequantize of that copy in one pass
+struct QdqArgs {
+  const void* x;
+  int in_dtype;    // 0 BF16, 1 FP32
+  int64_t M, K;
+  int amax_mode;   // 0 TENSOR, 1 LINE
+  const float* amax;
+  float F, F_inv;
+  uint8_t *q, *sc;  // both or neither
+  void* y;
+  int out_dtype;   // 0 BF16, 1 FP32
+  const float* noop;
+};
+int launch_qdq(const QdqArgs& a, hipStream_t s);
+
 }  // namespace nvfp4

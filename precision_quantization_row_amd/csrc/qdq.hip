@@ -1,0 +1,212 @@
+// qdq.hip -- rowwise quantize and the dequantize of that copy in one pass
+// (gfx950).
+//
+// The backward-overrides PR description's "dequantized" policy keeps the
+// rowwise fprop codes and scales and runs the backward GEMMs in BF16 on their
+// dequantization. Emitting that BF16 operand in the quantize pass reads X
+// once instead of reading X, then the codes again:
+//   codes, scales: the rowwise copy of X (1x16 blocks, per-tensor or
+//                  per-row amax), as nvfp4_quantize_transpose writes it
+//   y_k = RN(e2m1(code_k) * D), D = RN(RN(e4m3(byte) * a) * F_inv), the
+//         block's decode scale; BF16 output = RNE of the FP32 y_k
+// Rows are independent, so no LDS and no transpose: a lane holds 8
+// consecutive elements, a lane pair one 1x16 block.
+#include "nvfp4_device.h"
+#include "nvfp4_launch.h"
+
+#include <algorithm>
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Two E2M1 codes (byte SEL of w, low nibble first) -> two floats, exact
+// (v_cvt_scalef32_pk_f32_fp4 with scale 1.0 equals the E2M1 table for every
+// byte and select, checked on gfx950).
+template <int SEL>
+__device__ __forceinline__ f32x2 qdq_fp4x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// Two floats -> two BF16, round to nearest even (v_cvt_pk_bf16_f32, equal to
+// the RNE definition for every non-NaN fp32, checked on gfx950).
+__device__ __forceinline__ uint32_t qdq_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Vector path: K % 16 == 0 and aligned rows (x and y 16 bytes, codes 4
+// bytes). Workgroup tiles are (row, chunk of 256 x 8 columns); lane t of a
+// tile holds columns c .. c + 7, c = chunk * 2048 + 8 t. The two lanes of a
+// block are both inside the row or both past it (K % 16 == 0), so the DPP
+// swap that joins their maxima always reads an active lane.
+template <typename T, bool OUT_BF16, bool CODES>
+__global__ void __launch_bounds__(256) qdq_vec_kernel(const QdqArgs p, int64_t nchunk) {
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+  const int64_t K = p.K, qrs = K / 2, srs = K / 16;
+  const int64_t total = p.M * nchunk;
+  const int tid = threadIdx.x, par = tid & 1;
+  for (int64_t tile = blockIdx.x; tile < total; tile += gridDim.x) {
+    const int64_t r = tile / nchunk;
+    const int64_t c = (tile - r * nchunk) * 2048 + 8 * (int64_t)tid;
+    if (c >= K) continue;
+    const float a = p.amax_mode == 0 ? p.amax[0] : p.amax[r];
+    const float s_enc = global_encode_scale(a, p.F);
+    float v[8];
+    uint32_t m;
+    if constexpr (sizeof(T) == 2) {
+      const u32x4 w = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p.x) + r * K + c));
+      const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+      uint32_t t = 0u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[2 * k] = bf16_lo(d[k]);
+        v[2 * k + 1] = bf16_hi(d[k]);
+        t = pk_max_u16(t, d[k] & kAbsBf16x2);
+      }
+      m = max(t & 0xFFFFu, t >> 16) << 16;
+    } else {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const float*>(p.x) + r * K + c);
+      const u32x4 w0 = __builtin_nontemporal_load(src), w1 = __builtin_nontemporal_load(src + 1);
+      const uint32_t d[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      m = 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        v[k] = __uint_as_float(d[k]);
+        m = max(m, d[k] & kAbsF32);
+      }
+    }
+    m = max(m, dpp_swap1(m));
+    uint32_t byte;
+    float enc, dec;
+    block_scale_dec(__uint_as_float(m), a, s_enc, p.F_inv, &byte, &enc, &dec);
+    const uint32_t code = e2m1_pack8(v[0] * enc, v[1] * enc, v[2] * enc, v[3] * enc, v[4] * enc,
+                                     v[5] * enc, v[6] * enc, v[7] * enc);
+    if constexpr (CODES) {
+      *reinterpret_cast<uint32_t*>(p.q + r * qrs + c / 2) = code;
+      if (par == 0) p.sc[r * srs + c / 16] = (uint8_t)byte;
+    }
+    const f32x2 y0 = qdq_fp4x2<0>(code), y1 = qdq_fp4x2<1>(code);
+    const f32x2 y2 = qdq_fp4x2<2>(code), y3 = qdq_fp4x2<3>(code);
+    if constexpr (OUT_BF16) {
+      const u32x4 o = {qdq_bf16x2(y0.x * dec, y0.y * dec), qdq_bf16x2(y1.x * dec, y1.y * dec),
+                       qdq_bf16x2(y2.x * dec, y2.y * dec), qdq_bf16x2(y3.x * dec, y3.y * dec)};
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.y) + r * K + c));
+    } else {
+      u32x4* dst = reinterpret_cast<u32x4*>(static_cast<float*>(p.y) + r * K + c);
+      const u32x4 o0 = {__float_as_uint(y0.x * dec), __float_as_uint(y0.y * dec),
+                        __float_as_uint(y1.x * dec), __float_as_uint(y1.y * dec)};
+      const u32x4 o1 = {__float_as_uint(y2.x * dec), __float_as_uint(y2.y * dec),
+                        __float_as_uint(y3.x * dec), __float_as_uint(y3.y * dec)};
+      __builtin_nontemporal_store(o0, dst);
+      __builtin_nontemporal_store(o1, dst + 1);
+    }
+  }
+}
+
+// General path: any K and alignment. One thread per 1x16 block with bounds on
+// every element; a short last block uses only the elements that exist.
+template <typename T, bool OUT_BF16>
+__global__ void __launch_bounds__(256) qdq_kernel(const QdqArgs p) {
+  if (p.noop != nullptr && *p.noop == 1.0f) return;
+  const int64_t K = p.K, nb = (K + 15) / 16, qrs = (K + 1) / 2;
+  const int64_t total = p.M * nb;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t r = t / nb, b = t - r * nb, c0 = 16 * b;
+    const int n = (int)min((int64_t)16, K - c0);
+    const float a = p.amax_mode == 0 ? p.amax[0] : p.amax[r];
+    float v[16];
+    uint32_t m = 0u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[k] = 0.0f;
+      if (k < n) {
+        if constexpr (sizeof(T) == 2)
+          v[k] = __uint_as_float((uint32_t)static_cast<const uint16_t*>(p.x)[r * K + c0 + k] << 16);
+        else
+          v[k] = static_cast<const float*>(p.x)[r * K + c0 + k];
+      }
+      m = max(m, __float_as_uint(v[k]) & kAbsF32);
+    }
+    uint32_t byte;
+    float enc, dec;
+    block_scale_dec(__uint_as_float(m), a, global_encode_scale(a, p.F), p.F_inv, &byte, &enc, &dec);
+    const uint32_t w0 = e2m1_pack8(v[0] * enc, v[1] * enc, v[2] * enc, v[3] * enc, v[4] * enc,
+                                   v[5] * enc, v[6] * enc, v[7] * enc);
+    const uint32_t w1 = e2m1_pack8(v[8] * enc, v[9] * enc, v[10] * enc, v[11] * enc, v[12] * enc,
+                                   v[13] * enc, v[14] * enc, v[15] * enc);
+    if (p.q != nullptr) {
+      p.sc[r * nb + b] = (uint8_t)byte;
+      uint8_t* q = p.q + r * qrs + c0 / 2;
+      for (int j = 0; j < 8; ++j) {
+        if (2 * j >= n) break;
+        uint32_t bt = ((j < 4 ? w0 : w1) >> (8 * (j & 3))) & 0xFFu;
+        if (2 * j + 1 >= n) bt &= 0x0Fu;  // a missing last high nibble is 0
+        q[j] = (uint8_t)bt;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = j < 4 ? w0 : w1;
+      f32x2 e;
+      switch (j & 3) {
+        case 0: e = qdq_fp4x2<0>(w); break;
+        case 1: e = qdq_fp4x2<1>(w); break;
+        case 2: e = qdq_fp4x2<2>(w); break;
+        default: e = qdq_fp4x2<3>(w); break;
+      }
+      const float ya = e.x * dec, yb = e.y * dec;
+      for (int h = 0; h < 2; ++h) {
+        const int k = 2 * j + h;
+        if (k >= n) break;
+        const float yv = h ? yb : ya;
+        if constexpr (OUT_BF16) {
+          const uint32_t bits = __float_as_uint(yv);
+          static_cast<uint16_t*>(p.y)[r * K + c0 + k] =
+              (uint16_t)((bits + 0x7FFFu + ((bits >> 16) & 1u)) >> 16);
+        } else {
+          static_cast<float*>(p.y)[r * K + c0 + k] = yv;
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+static int launch_qdq_t(const QdqArgs& a, hipStream_t s) {
+  const bool codes = a.q != nullptr;
+  const bool vec = (a.K % 16 == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(a.y) & 15) == 0) &&
+                   (!codes || (reinterpret_cast<uintptr_t>(a.q) & 3) == 0);
+  if (vec) {
+    const int64_t nchunk = (a.K + 2047) / 2048;
+    const int64_t blocks =
+        std::max<int64_t>(1, std::min<int64_t>(a.M * nchunk, (int64_t)num_cus() * 8));
+    const dim3 g((unsigned)blocks), b(256);
+    if (a.out_dtype == 0) {
+      if (codes) hipLaunchKernelGGL((qdq_vec_kernel<T, true, true>), g, b, 0, s, a, nchunk);
+      else hipLaunchKernelGGL((qdq_vec_kernel<T, true, false>), g, b, 0, s, a, nchunk);
+    } else {
+      if (codes) hipLaunchKernelGGL((qdq_vec_kernel<T, false, true>), g, b, 0, s, a, nchunk);
+      else hipLaunchKernelGGL((qdq_vec_kernel<T, false, false>), g, b, 0, s, a, nchunk);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+  }
+  const int64_t total = a.M * ((a.K + 15) / 16);
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((total + 255) / 256, (int64_t)num_cus() * 16));
+  if (a.out_dtype == 0)
+    hipLaunchKernelGGL((qdq_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((qdq_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_qdq(const QdqArgs& a, hipStream_t s) {
+  return a.in_dtype == 0 ? launch_qdq_t<uint16_t>(a, s) : launch_qdq_t<float>(a, s);
+}
+
+}  // namespace nvfp4

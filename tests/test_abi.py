@@ -97,6 +97,13 @@ def test_validation_rejects_before_launch():
     assert d(bound=500.0) == E
     assert d(R=0) == E
     assert d(C=0) == E
+    # quantize-dequantize: missing input / amax / output, half a copy, modes, dtypes
+    qd = lambda M=32, K=32, x=_fake(), ra=_fake(), y=_fake(), qr=_fake(), sr=_fake(), mode=1, \
+        dt=0, od=0, bound=448.0: lib.nvfp4_quantize_dequantize(x, dt, M, K, mode, ra, f(bound), qr,
+                                                                sr, y, od, None, None)
+    for kw in (dict(M=0), dict(K=0), dict(x=None), dict(ra=None), dict(y=None), dict(sr=None),
+               dict(qr=None), dict(mode=2), dict(dt=5), dict(od=5), dict(bound=-1.0)):
+        assert qd(**kw) == E, kw
     # 2-D blocks: missing amax / buffers, sizes, bound, dtype
     t = lambda M=32, K=32, ta=_fake(), bound=448.0, qr=_fake(), sr=_fake(), qc=_fake(), sc=_fake(), \
         dt=0, x=_fake(): lib.nvfp4_quantize_2d(x, dt, M, K, ta, f(bound), qr, sr, qc, sc, None, None)
