@@ -136,6 +136,35 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
   }
 }
 
+// Magnitude bits of the largest element in one 16-byte vector (BF16: the
+// larger half shifted into fp32 position).
+template <typename T>
+__device__ __forceinline__ uint32_t vec_max_bits(const uint4 v) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t t = pk_max_u16(pk_max_u16(v.x & kAbsBf16x2, v.y & kAbsBf16x2),
+                                  pk_max_u16(v.z & kAbsBf16x2, v.w & kAbsBf16x2));
+    return max(t & 0xFFFFu, t >> 16) << 16;
+  } else {
+    return max(max(v.x & kAbsF32, v.y & kAbsF32), max(v.z & kAbsF32, v.w & kAbsF32));
+  }
+}
+
+// The lane's share of a row max over nv 16-byte vectors (lane, lane + 64, ...):
+// four independent loads in flight per iteration, so a wave that owns a row
+// keeps 4 KB of it on the way instead of 1 KB.
+template <typename T>
+__device__ __forceinline__ uint32_t lane_row_max(const uint4* __restrict__ rv, int64_t nv, int lane) {
+  uint32_t m0 = 0u, m1 = 0u;
+  int64_t i = lane;
+  for (; i + 192 < nv; i += 256) {
+    const uint4 a = rv[i], b = rv[i + 64], c = rv[i + 128], d = rv[i + 192];
+    m0 = max(m0, max(vec_max_bits<T>(a), vec_max_bits<T>(b)));
+    m1 = max(m1, max(vec_max_bits<T>(c), vec_max_bits<T>(d)));
+  }
+  for (; i < nv; i += 64) m0 = max(m0, vec_max_bits<T>(rv[i]));
+  return max(m0, m1);
+}
+
 // -------------------------------------------------------------- row amax
 // One wave per row (grid-stride over rows); lanes stride the row with 16-byte
 // vectors when every row starts 16-byte aligned, else with scalar loads. The
@@ -153,18 +182,8 @@ __global__ void __launch_bounds__(256) row_amax_kernel(const T* __restrict__ x, 
     const T* row = x + r * K;
     uint32_t m = 0u;
     if (VEC) {
-      const uint4* rv = reinterpret_cast<const uint4*>(row);
       const int64_t nv = K / V;
-      for (int64_t i = lane; i < nv; i += 64) {
-        const uint4 v = rv[i];
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t t = pk_max_u16(pk_max_u16(v.x & kAbsBf16x2, v.y & kAbsBf16x2),
-                                        pk_max_u16(v.z & kAbsBf16x2, v.w & kAbsBf16x2));
-          m = max(m, max(t & 0xFFFFu, t >> 16) << 16);
-        } else {
-          m = max(m, max(max(v.x & kAbsF32, v.y & kAbsF32), max(v.z & kAbsF32, v.w & kAbsF32)));
-        }
-      }
+      m = lane_row_max<T>(reinterpret_cast<const uint4*>(row), nv, lane);
       for (int64_t i = nv * V + lane; i < K; i += 64) {  // K % V tail (never with VEC rows)
         if constexpr (sizeof(T) == 2)
           m = max(m, (uint32_t)(reinterpret_cast<const uint16_t*>(row)[i] & 0x7FFFu) << 16);
@@ -337,17 +356,7 @@ __global__ void __launch_bounds__(256) grouped_row_amax_kernel(const T* __restri
     const T* row = x + r * K;
     uint32_t m = 0u;
     if (VEC) {
-      const uint4* rv = reinterpret_cast<const uint4*>(row);
-      for (int64_t i = lane; i < K / V; i += 64) {
-        const uint4 v = rv[i];
-        if constexpr (sizeof(T) == 2) {
-          const uint32_t t = pk_max_u16(pk_max_u16(v.x & kAbsBf16x2, v.y & kAbsBf16x2),
-                                        pk_max_u16(v.z & kAbsBf16x2, v.w & kAbsBf16x2));
-          m = max(m, max(t & 0xFFFFu, t >> 16) << 16);
-        } else {
-          m = max(m, max(max(v.x & kAbsF32, v.y & kAbsF32), max(v.z & kAbsF32, v.w & kAbsF32)));
-        }
-      }
+      m = lane_row_max<T>(reinterpret_cast<const uint4*>(row), K / V, lane);
     } else {
       for (int64_t i = lane; i < K; i += 64) {
         if constexpr (sizeof(T) == 2)
