@@ -132,3 +132,21 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(16, 16, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         p.nvfp4_amax_rowcol(x, torch.zeros(16))
+
+
+def test_padded_rows_max_bounds_every_layout():
+    """The binding's worst-case M_out for grouped tokens covers every split of
+    T tokens into G groups (the header's sizing rule)."""
+    import numpy as np
+    import oracle
+    rng = np.random.RandomState(3)
+    for _ in range(200):
+        G = int(rng.randint(1, 20))
+        align = 16 * int(rng.randint(1, 9))
+        rows = rng.multinomial(int(rng.randint(0, 500)), np.ones(G) / G)
+        T = int(rows.sum())
+        need = int(oracle.padded_group_end(rows, align, 1 << 40)[-1])
+        bound = p.padded_rows_max(T, G, align)
+        assert need <= bound and bound % align == 0
+    # the bound is reached: every group one row past a multiple of align
+    assert p.padded_rows_max(3 * 17, 3, 16) == int(oracle.padded_group_end([17, 17, 17], 16, 1 << 40)[-1])
