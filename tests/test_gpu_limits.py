@@ -79,3 +79,43 @@ def test_rows_past_the_interior_offset_limit(dtype, K):
     qc, sc = oracle.quantize_colwise(xc, oracle.MODE_LINE, ac, 448.0)
     assert_same("q_col[sampled]", to_np(out["q_col"][cols]), qc)
     assert_same("s_col[sampled]", to_np(out["s_col"][cols]), sc)
+
+
+@pytest.mark.parametrize("dtype,K", [(torch.bfloat16, (1 << 25) + 256), (torch.float32, (1 << 24) + 256)])
+def test_2d_and_quantize_dequantize_past_the_offset_limit(dtype, K):
+    """The 2-D tile cast and the one-pass quantize + dequantize on the same
+    wide rows: sampled 16 x 16 tiles and whole sampled rows against the oracle."""
+    M = 64
+    say(f"[gpu] limits 2-D / qdq: {M}x{K} {dtype}")
+    x = _wide_matrix(M, K, dtype, seed=23 if dtype == torch.bfloat16 else 24)
+    ta = torch.empty(1, device=DEV)
+    p.nvfp4_amax_rowcol(x, None, None, ta)
+    out = p.empty_outputs(M, K, DEV)
+    for v in out.values():
+        v.fill_(0xA5)
+    p.nvfp4_quantize_2d(x, ta, 448.0, out["q_row"], out["s_row"], out["q_col"], out["s_col"])
+    torch.cuda.synchronize()
+    a = np.float32(ta.item())
+    for r0, c0 in [(0, 0), (16, 1 << 20), (48, K - 256), (32, K - 16)]:
+        xt = x[r0:r0 + 16, c0:c0 + 16].float().cpu().numpy()
+        q, s, qc, sc = oracle.quantize_2d(xt, a, 448.0)
+        assert_same(f"2d q_row tile ({r0},{c0})", to_np(out["q_row"][r0:r0 + 16, c0 // 2:c0 // 2 + 8]), q)
+        assert_same(f"2d s_row tile ({r0},{c0})", to_np(out["s_row"][r0:r0 + 16, c0 // 16:c0 // 16 + 1]), s)
+        assert_same(f"2d q_col tile ({r0},{c0})", to_np(out["q_col"][c0:c0 + 16, r0 // 2:r0 // 2 + 8]), qc)
+        assert_same(f"2d s_col tile ({r0},{c0})", to_np(out["s_col"][c0:c0 + 16, r0 // 16:r0 // 16 + 1]), sc)
+    del out
+    ra = torch.empty(M, device=DEV)
+    p.nvfp4_amax_rowcol(x, ra)
+    y = torch.empty(M, K, dtype=torch.bfloat16, device=DEV)
+    qr = torch.empty(M, (K + 1) // 2, dtype=torch.uint8, device=DEV)
+    sr = torch.empty(M, (K + 15) // 16, dtype=torch.uint8, device=DEV)
+    p.nvfp4_quantize_dequantize(x, p.NVFP4_AMAX_LINE, ra, 448.0, y, qr, sr)
+    torch.cuda.synchronize()
+    for r in (1, M - 1):
+        xr = x[r:r + 1].float().cpu().numpy()
+        ar = oracle.amax_rows(xr)
+        wq, ws, wy = oracle.quantize_dequantize(xr, oracle.MODE_LINE, ar, 448.0)
+        assert_same(f"qdq q_row[{r}]", to_np(qr[r:r + 1]), wq)
+        assert_same(f"qdq s_row[{r}]", to_np(sr[r:r + 1]), ws)
+        assert_same(f"qdq y[{r}]", y[r:r + 1].view(torch.int16).cpu().numpy().view(np.uint16),
+                    oracle.to_bf16_bits(wy))
