@@ -161,6 +161,42 @@ __device__ __forceinline__ void load_row_buf(__amdgpu_buffer_rsrc_t rx, uint32_t
 }
 
 // ------------------------------------------------------------------ stores
+// Eight bytes to any address as naturally aligned pieces (one 8-byte store
+// when the address allows, else 2-4 stores of 4, 2 and 1 bytes). A lane's
+// columns c + k have c % 8 == 0, so for one k the address alignment is the
+// same on every lane and the branch is uniform.
+__device__ __forceinline__ void store8_pieces(uint8_t* dst, uint32_t w0, uint32_t w1) {
+  const uint64_t v = (uint64_t)w0 | ((uint64_t)w1 << 32);
+  switch (reinterpret_cast<uintptr_t>(dst) & 7) {
+    case 0:
+      *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+      break;
+    case 4:
+      reinterpret_cast<uint32_t*>(dst)[0] = w0;
+      reinterpret_cast<uint32_t*>(dst)[1] = w1;
+      break;
+    case 2:
+    case 6:
+      *reinterpret_cast<uint16_t*>(dst) = (uint16_t)v;
+      *reinterpret_cast<uint32_t*>(dst + 2) = (uint32_t)(v >> 16);
+      *reinterpret_cast<uint16_t*>(dst + 6) = (uint16_t)(v >> 48);
+      break;
+    case 1:
+    case 5:
+      dst[0] = (uint8_t)v;
+      *reinterpret_cast<uint16_t*>(dst + 1) = (uint16_t)(v >> 8);
+      *reinterpret_cast<uint32_t*>(dst + 3) = (uint32_t)(v >> 24);
+      dst[7] = (uint8_t)(v >> 56);
+      break;
+    default:  // 3, 7
+      dst[0] = (uint8_t)v;
+      *reinterpret_cast<uint32_t*>(dst + 1) = (uint32_t)(v >> 8);
+      *reinterpret_cast<uint16_t*>(dst + 5) = (uint16_t)(v >> 40);
+      dst[7] = (uint8_t)(v >> 56);
+      break;
+  }
+}
+
 // Edge: global stores with bounds and alignment checks per element.
 struct StoreChecked {
   uint8_t *q_row, *s_row, *q_col, *s_col;
@@ -191,6 +227,8 @@ struct StoreChecked {
     uint8_t* dst = q_col + cc * qcs + rb0 / 2;
     if (col8 && rb0 + 16 <= re) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+    } else if (rb0 + 16 <= re) {
+      store8_pieces(dst, w0, w1);
     } else {
 #pragma unroll
       for (int b = 0; b < 8; ++b)
