@@ -139,3 +139,8 @@ def test_2d_full_size_sampled_bands():
         assert_same(f"s_row band {band}", to_np(out["s_row"][r0:r0 + 16]), ws)
         assert_same(f"q_col band {band}", to_np(out["q_col"][:, r0 // 2:r0 // 2 + 8]), wqc)
         assert_same(f"s_col band {band}", to_np(out["s_col"][:, band:band + 1]), wsc)
+
+
+@pytest.mark.parametrize("M,K", [(256, 320), (512, 2880)])
+def test_2d_columns_past_the_last_strip(M, K):
+    _check("partial strip", _matrix(M, K, torch.bfloat16, seed=M + K))

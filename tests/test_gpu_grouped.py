@@ -158,7 +158,8 @@ def _round64(n):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("case", ["mixed", "large_align", "short_x", "truncated", "many", "past"])
+@pytest.mark.parametrize("case", ["mixed", "large_align", "short_x", "truncated", "many", "past",
+                                  "partial_strip"])
 def test_macro_tile_layouts(dtype, case):
     """Layouts that take the macro-tile path (K a multiple of 256, M_out of 64):
     16-row blocks that end a group mid-block, next to padding, empty groups,
@@ -173,6 +174,8 @@ def test_macro_tile_layouts(dtype, case):
         group_rows, align, T = [200, 200], 32, 150
     elif case == "truncated":
         group_rows = [300, 300]
+    elif case == "partial_strip":
+        group_rows, K = [100, 37, 0, 60], 320
     elif case == "many":
         group_rows = np.random.RandomState(17).randint(0, 41, size=p.NVFP4_GROUPS_MAX).tolist()
     else:

@@ -249,3 +249,37 @@ def test_other_stream():
     xf = w.x.float().numpy()
     q, sc = oracle.quantize_colwise(xf, 1, oracle.amax_cols(xf), 448.0)
     assert_same("q_col", to_np(out["q_col"]), q)
+
+
+# ------------------------------------ macro tiles with a partial last strip
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("M,K", [(256, 320), (512, 2880), (320, 576), (384, 1088)])
+def test_interior_with_columns_past_the_last_strip(dtype, M, K):
+    """K % 256 != 0 (K % 64 == 0): the macro-tile kernel takes the whole
+    256-column strips and the edge kernel the remaining columns (and the
+    rows below the last macro tile); every output byte against the oracle,
+    both directions and each direction alone, per-row and per-tensor."""
+    w = workloads.make("llm_mlp", (M, K))
+    x_cpu = w.x.to(dtype)
+    check_row_scaled(x_cpu, bounds=(448.0,), dequant=False, label="partial strip")
+    x = x_cpu.to(DEV)
+    xf = x_cpu.float().numpy()
+    ra, ca, ta = gpu_amax(x, tensor=True)
+    for rw, cw in ((True, False), (False, True)):
+        out = gpu_quantize(x, p.NVFP4_AMAX_LINE, ra, p.NVFP4_AMAX_LINE, ca, 256.0, rowwise=rw, colwise=cw)
+        if rw:
+            q, s = oracle.quantize_rowwise(xf, oracle.MODE_LINE, oracle.amax_rows(xf), 256.0)
+            assert_same("q_row", to_np(out["q_row"]), q)
+            assert_same("s_row", to_np(out["s_row"]), s)
+        if cw:
+            q, s = oracle.quantize_colwise(xf, oracle.MODE_LINE, oracle.amax_cols(xf), 256.0)
+            assert_same("q_col", to_np(out["q_col"]), q)
+            assert_same("s_col", to_np(out["s_col"]), s)
+    a = [oracle.amax_tensor(xf)]
+    out = gpu_quantize(x, p.NVFP4_AMAX_TENSOR, ta, p.NVFP4_AMAX_TENSOR, ta, 448.0)
+    q, s = oracle.quantize_rowwise(xf, oracle.MODE_TENSOR, a, 448.0)
+    qc, sc = oracle.quantize_colwise(xf, oracle.MODE_TENSOR, a, 448.0)
+    assert_same("q_row tensor", to_np(out["q_row"]), q)
+    assert_same("s_row tensor", to_np(out["s_row"]), s)
+    assert_same("q_col tensor", to_np(out["q_col"]), qc)
+    assert_same("s_col tensor", to_np(out["s_col"]), sc)
