@@ -248,22 +248,40 @@ __global__ void __launch_bounds__(256) col_amax_kernel(const T* __restrict__ x, 
 #pragma unroll
   for (int k = 0; k < V; ++k) m[k] = 0u;
   const int64_t c = c0 + (int64_t)lane * V;
+  // one 16-byte vector of a row into the lane's running column maxima
+  auto take = [&](const uint4 v) {
+    if constexpr (VEC) {
+      const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          m[2 * d] = max(m[2 * d], (dw[d] & 0x7FFFu) << 16);
+          m[2 * d + 1] = max(m[2 * d + 1], dw[d] & 0x7FFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) m[d] = max(m[d], dw[d] & kAbsF32);
+      }
+    }
+  };
   if (c < K) {
-    for (int64_t r = rs + w; r < re; r += 4) {
+    int64_t r = rs + w;
+    if constexpr (VEC) {  // four rows in flight per wave
+      for (; r + 12 < re; r += 16) {
+        const uint4 a = *reinterpret_cast<const uint4*>(x + r * K + c);
+        const uint4 b = *reinterpret_cast<const uint4*>(x + (r + 4) * K + c);
+        const uint4 d = *reinterpret_cast<const uint4*>(x + (r + 8) * K + c);
+        const uint4 e = *reinterpret_cast<const uint4*>(x + (r + 12) * K + c);
+        take(a);
+        take(b);
+        take(d);
+        take(e);
+      }
+    }
+    for (; r < re; r += 4) {
       const T* p = x + r * K + c;
       if constexpr (VEC) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
-        const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            m[2 * d] = max(m[2 * d], (dw[d] & 0x7FFFu) << 16);
-            m[2 * d + 1] = max(m[2 * d + 1], dw[d] & 0x7FFF0000u);
-          }
-        } else {
-#pragma unroll
-          for (int d = 0; d < 4; ++d) m[d] = max(m[d], dw[d] & kAbsF32);
-        }
+        take(*reinterpret_cast<const uint4*>(p));
       } else {
         if constexpr (sizeof(T) == 2)
           m[0] = max(m[0], (uint32_t)(*reinterpret_cast<const uint16_t*>(p) & 0x7FFFu) << 16);
