@@ -315,16 +315,17 @@ __global__ void __launch_bounds__(256) tensor_amax_kernel(const T* __restrict__ 
   if (VEC) {
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     const int64_t nv = n / V;
-    for (int64_t i = t0; i < nv; i += stride) {
-      const uint4 v = xv[i];
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t t = pk_max_u16(pk_max_u16(v.x & kAbsBf16x2, v.y & kAbsBf16x2),
-                                      pk_max_u16(v.z & kAbsBf16x2, v.w & kAbsBf16x2));
-        m = max(m, max(t & 0xFFFFu, t >> 16) << 16);
-      } else {
-        m = max(m, max(max(v.x & kAbsF32, v.y & kAbsF32), max(v.z & kAbsF32, v.w & kAbsF32)));
-      }
+    // a wave reads 64 x 16 B per load; four loads of consecutive 1 KB pieces
+    // are in flight per wave and iteration
+    const int64_t lane = threadIdx.x & 63, wave = t0 >> 6, nwaves = stride >> 6;
+    int64_t i = wave * 256 + lane;
+    for (; i + 192 < nv; i += nwaves * 256) {
+      const uint4 a = xv[i], b = xv[i + 64], c = xv[i + 128], d = xv[i + 192];
+      m = max(m, max(max(vec_max_bits<T>(a), vec_max_bits<T>(b)),
+                     max(vec_max_bits<T>(c), vec_max_bits<T>(d))));
     }
+    // a lane stops early only in the last, partial group: the rest of it
+    for (; i < nv; i += 64) m = max(m, vec_max_bits<T>(xv[i]));
     done = nv * V;
   }
   for (int64_t i = done + t0; i < n; i += stride) {
