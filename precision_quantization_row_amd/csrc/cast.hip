@@ -344,6 +344,50 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_sel(uint32_t old, float v0, float 
   }
 }
 
+// Packed maximum of three dwords of two 16-bit magnitude patterns each. With
+// F16, one v_pk_maximum3_f16 (the patterns compared as f16 numbers: the same
+// order as integers for patterns below 0x7C00, an f16 infinity or NaN above);
+// otherwise two integer v_pk_max_u16.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <bool F16>
+__device__ __forceinline__ uint32_t pk_max3_mag(uint32_t a, uint32_t b, uint32_t c) {
+  if constexpr (F16) {
+    const f16x2 x = __builtin_bit_cast(f16x2, a), y = __builtin_bit_cast(f16x2, b),
+                z = __builtin_bit_cast(f16x2, c);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_maximum(
+                                            __builtin_elementwise_maximum(x, y), z));
+  } else {
+    return pk_max_u16(pk_max_u16(a, b), c);
+  }
+}
+
+// Block maxima of a BF16 16 x 8 lane block: cm[d] = packed maxima over the 16
+// rows of the lane's columns 2d, 2d + 1; rb[i] = packed maxima of row i over
+// its even and its odd columns. F16 selects the three-input compare above.
+template <bool F16, bool ROWW, bool COLW>
+__device__ __forceinline__ void maxima_bf16(const uint32_t (&w)[16][4], uint32_t (&cm)[4],
+                                            uint32_t (&rb)[16]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) cm[d] = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    uint32_t a[4], b[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      a[d] = w[i][d] & kAbsBf16x2;
+      b[d] = w[i + 1][d] & kAbsBf16x2;
+    }
+    if constexpr (COLW) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) cm[d] = pk_max3_mag<F16>(cm[d], a[d], b[d]);
+    }
+    if constexpr (ROWW) {
+      rb[i] = pk_max_u16(pk_max3_mag<F16>(a[0], a[1], a[2]), a[3]);
+      rb[i + 1] = pk_max_u16(pk_max3_mag<F16>(b[0], b[1], b[2]), b[3]);
+    }
+  }
+}
+
 // The same two directions as process_block, in three batched phases, so that
 // independent work sits side by side for the scheduler:
 //   1. every block maximum of the 16 x 8 block (integer max on magnitudes);
@@ -358,27 +402,31 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
                                                       const RowTab& row, const ColTab& col,
                                                       float f_inv, const Mid& mid) {
   constexpr int NW = Blk<T>::NW;
-  // ---- phase 1: maxima
+  // ---- phase 1: maxima. BF16: cm[d] holds the packed column maxima of
+  // dword d, rb[i] the packed maxima of row i's even and odd columns (folded
+  // after the exchange with the lane pair). FP32: plain magnitude bits.
   uint32_t cm[NW];
   uint32_t rb[16];
-#pragma unroll
-  for (int d = 0; d < NW; ++d) cm[d] = 0u;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t a0 = w[i][0] & kAbsBf16x2, a1 = w[i][1] & kAbsBf16x2;
-      const uint32_t a2 = w[i][2] & kAbsBf16x2, a3 = w[i][3] & kAbsBf16x2;
-      if constexpr (COLW) {
-        cm[0] = pk_max_u16(cm[0], a0);
-        cm[1] = pk_max_u16(cm[1], a1);
-        cm[2] = pk_max_u16(cm[2], a2);
-        cm[3] = pk_max_u16(cm[3], a3);
-      }
-      if constexpr (ROWW) {
-        const uint32_t t = pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3));
-        rb[i] = max(t & 0xFFFFu, t >> 16) << 16;
-      }
+  if constexpr (sizeof(T) == 2) {
+    maxima_bf16<true, ROWW, COLW>(w, cm, rb);
+    // The fast form compares BF16 magnitudes as f16 numbers, which orders
+    // them like integers unless a pattern reads as an f16 infinity or NaN
+    // (magnitudes >= 2^121). The column maxima cover every element (the row
+    // maxima do when there is no column direction); if any of them reached
+    // that range the lane redoes the maxima with integer compares.
+    uint32_t m = 0u;
+    if constexpr (COLW) {
+      m = pk_max_u16(pk_max_u16(cm[0], cm[1]), pk_max_u16(cm[2], cm[3]));
     } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m = pk_max_u16(m, rb[i]);
+    }
+    if (max(m & 0xFFFFu, m >> 16) >= 0x7C00u) maxima_bf16<false, ROWW, COLW>(w, cm, rb);
+  } else {
+#pragma unroll
+    for (int d = 0; d < NW; ++d) cm[d] = 0u;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
       uint32_t m = 0u;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -391,55 +439,92 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
   }
   mid();
 
-  // ---- phase 2: scales. All 16 take the unguarded fast form; a lane where
-  // any of them falls outside its range (tiny blocks, extreme decode scales)
-  // redoes all of its scales with the guarded form.
+  // ---- phase 2: scales. The lane's line amaxes and S_enc values are read
+  // from their tables first, all 16 chains take the unguarded form, and one
+  // range check over all of them (smallest block max, smallest and largest
+  // D) decides; a lane outside either range (tiny blocks, extreme decode
+  // scales) redoes all of its scales with the guarded form and stages its
+  // scale bytes again.
   float renc[8];  // encode factor of this lane's row 2j + par
+  float cenc[8];
   uint32_t bsel[8];
-  bool ok = true;
+  float ta[8], ts[8], tca[8], tcs[8];
   if constexpr (ROWW) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t b0 = max(rb[2 * j], dpp_swap1(rb[2 * j]));
-      const uint32_t b1 = max(rb[2 * j + 1], dpp_swap1(rb[2 * j + 1]));
-      bsel[j] = par ? b1 : b0;
-      const int lr = 16 * g + 2 * j + par;
-      uint32_t byte;
-      ok &= block_scale_fast(__uint_as_float(bsel[j]), row.a(lr), row.s(lr), f_inv, &byte, &renc[j]);
-      st.row_scale(j, byte);
+      ta[j] = row.a(16 * g + 2 * j + par);
+      ts[j] = row.s(16 * g + 2 * j + par);
     }
   }
-  float cenc[8];
+  if constexpr (COLW) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      tca[k] = col.a(k);
+      tcs[k] = col.s(k);
+    }
+  }
   auto col_bits = [&](int k) -> uint32_t {
     if constexpr (sizeof(T) == 2)
       return (k & 1) ? (cm[k >> 1] & 0xFFFF0000u) : (cm[k >> 1] << 16);
     else
       return cm[k];
   };
+  uint32_t bmin = 0xFFFFFFFFu, dmin = 0xFFFFFFFFu, dmax = 0u;
+  if constexpr (ROWW) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      // the lane sends its partner the maximum of the partner's row and takes
+      // the partner's maximum of its own row: one swap per row pair
+      const uint32_t mine = par ? rb[2 * j + 1] : rb[2 * j];
+      const uint32_t other = par ? rb[2 * j] : rb[2 * j + 1];
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t u = pk_max_u16(mine, dpp_swap1(other));
+        bsel[j] = max(u & 0xFFFFu, u >> 16) << 16;
+      } else {
+        bsel[j] = max(mine, dpp_swap1(other));
+      }
+      uint32_t byte;
+      const uint32_t db =
+          block_scale_unchecked(__uint_as_float(bsel[j]), ta[j], ts[j], f_inv, &byte, &renc[j]);
+      st.row_scale(j, byte);
+      bmin = min(bmin, bsel[j]);
+      dmin = min(dmin, db);
+      dmax = max(dmax, db);
+    }
+  }
   if constexpr (COLW) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       uint32_t byte;
-      ok &= block_scale_fast(__uint_as_float(col_bits(k)), col.a(k), col.s(k), f_inv, &byte,
-                             &cenc[k]);
+      const uint32_t db = block_scale_unchecked(__uint_as_float(col_bits(k)), tca[k], tcs[k], f_inv,
+                                                &byte, &cenc[k]);
       st.col_scale(k, byte);
+      bmin = min(bmin, col_bits(k));
+      dmin = min(dmin, db);
+      dmax = max(dmax, db);
     }
   }
+  // the fast forms hold for bamax >= 2^-125 and D in [2^-126, 2^126)
+  const bool ok = (bmin >= 0x01000000u) & (dmin >= 0x00800000u) & (dmax < 0x7E800000u);
   if (!ok) {
+    // The block maxima pass through an empty asm statement so that the
+    // compiler cannot share work between the two forms: sharing would keep
+    // the fast form's intermediates alive past their last fast use.
     if constexpr (ROWW) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int lr = 16 * g + 2 * j + par;
-        uint32_t byte;
-        block_scale(__uint_as_float(bsel[j]), row.a(lr), row.s(lr), f_inv, &byte, &renc[j]);
+        uint32_t byte, bm = bsel[j];
+        asm volatile("" : "+v"(bm));
+        block_scale(__uint_as_float(bm), ta[j], ts[j], f_inv, &byte, &renc[j]);
         st.row_scale(j, byte);
       }
     }
     if constexpr (COLW) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        uint32_t byte;
-        block_scale(__uint_as_float(col_bits(k)), col.a(k), col.s(k), f_inv, &byte, &cenc[k]);
+        uint32_t byte, bm = col_bits(k);
+        asm volatile("" : "+v"(bm));
+        block_scale(__uint_as_float(bm), tca[k], tcs[k], f_inv, &byte, &cenc[k]);
         st.col_scale(k, byte);
       }
     }

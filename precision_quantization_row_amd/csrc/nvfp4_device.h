@@ -98,6 +98,26 @@ __device__ __forceinline__ void block_scale(float bamax, float a, float s_enc, f
   *enc = (d == 0.0f) ? 0.0f : recip_rn(d);
 }
 
+// The unguarded scale chain itself: *byte (low byte) and *enc as block_scale
+// gives them whenever bamax >= 2^-125 and D lies in [2^-126, 2^126); returns
+// D's bit pattern so that callers can check that range for many blocks at once.
+// The converter keeps the upper half of its first operand's register, so it
+// starts from s32's own bits (no zeroing move); only the low byte is used.
+__device__ __forceinline__ uint32_t block_scale_unchecked(float bamax, float a, float s_enc,
+                                                          float f_inv, uint32_t* byte, float* enc) {
+  constexpr float kR6 = 0.16666667163372039794921875f;  // RN(1/6)
+  const float q0 = bamax * kR6;
+  const float q = __builtin_fmaf(__builtin_fmaf(-q0, kE2M1Max, bamax), kR6, q0);
+  const float s32 = fminf(q * s_enc, kE4M3Max);
+  const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(s32, s32, __float_as_int(s32), false);
+  *byte = (uint32_t)pk;
+  const float sq = __builtin_amdgcn_cvt_f32_fp8(pk, 0);
+  const float d = (sq * a) * f_inv;
+  const float r = __builtin_amdgcn_rcpf(d);
+  *enc = __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+  return __float_as_uint(d);
+}
+
 // block_scale without its range guards, for the batched block code: the same
 // results whenever bamax >= 2^-125 (div6_rn's fast form) and D lies in
 // [2^-126, 2^126) (recip_rn's fast form; then D != 0 too), which it reports.
@@ -105,17 +125,8 @@ __device__ __forceinline__ void block_scale(float bamax, float a, float s_enc, f
 // Callers redo the lanes where it returns false with block_scale.
 __device__ __forceinline__ bool block_scale_fast(float bamax, float a, float s_enc, float f_inv,
                                                  uint32_t* byte, float* enc) {
-  constexpr float kR6 = 0.16666667163372039794921875f;  // RN(1/6)
-  const float q0 = bamax * kR6;
-  const float q = __builtin_fmaf(__builtin_fmaf(-q0, kE2M1Max, bamax), kR6, q0);
-  const float s32 = fminf(q * s_enc, kE4M3Max);
-  const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(s32, s32, 0, false);
-  *byte = (uint32_t)pk;
-  const float sq = __builtin_amdgcn_cvt_f32_fp8(pk, 0);
-  const float d = (sq * a) * f_inv;
-  const float r = __builtin_amdgcn_rcpf(d);
-  *enc = __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
-  const uint32_t bb = __float_as_uint(bamax), db = __float_as_uint(d);
+  const uint32_t db = block_scale_unchecked(bamax, a, s_enc, f_inv, byte, enc);
+  const uint32_t bb = __float_as_uint(bamax);
   return (bb >= 0x01000000u) & ((db - 0x00800000u) < 0x7E000000u);
 }
 

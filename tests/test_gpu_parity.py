@@ -283,3 +283,46 @@ def test_interior_with_columns_past_the_last_strip(dtype, M, K):
     assert_same("s_row tensor", to_np(out["s_row"]), s)
     assert_same("q_col tensor", to_np(out["q_col"]), qc)
     assert_same("s_col tensor", to_np(out["s_col"]), sc)
+
+
+# ------------------------------------- BF16 magnitudes over the whole range
+def _bf16_exponent_sweep(M: int, K: int, seed: int = 11) -> torch.Tensor:
+    """N(0,1) rows scaled by 2^e with e swept over the BF16 range (subnormal
+    rows included), plus planted elements: single magnitudes in [2^121,
+    2^126] inside ordinary rows, a row of exactly 2^121, a row of BF16
+    subnormals and an all-zero row. Magnitudes of 2^121 and above are the
+    patterns that read as f16 infinities or NaNs."""
+    g = torch.Generator().manual_seed(seed)
+    z = torch.randn(M, K, generator=g)
+    e = torch.linspace(-140.0, 124.0, M).round()
+    x = z * torch.pow(2.0, e)[:, None]
+    idx = torch.randperm(M * K, generator=g)[: M * K // 997]
+    x.view(-1)[idx] = torch.pow(2.0, torch.randint(121, 127, (idx.numel(),), generator=g).float()) * \
+        torch.where(torch.rand(idx.numel(), generator=g) < 0.5, -1.0, 1.0)
+    x[M // 3] = 2.0 ** 121
+    x[M // 2] = torch.where(torch.rand(K, generator=g) < 0.5, -1.0, 1.0) * 2.0 ** -130
+    x[M // 5] = 0.0
+    xb = x.to(torch.bfloat16)
+    assert torch.isfinite(xb.float()).all()
+    return xb
+
+
+@pytest.mark.parametrize("M,K", [(512, 512), (256, 768)])
+def test_bf16_whole_exponent_range(M, K):
+    """Every output byte against the oracle for BF16 magnitudes from
+    subnormal to 2^126, through the macro-tile kernel: both directions and
+    each alone, bounds 448 and 256 (dequantize is left out: decode scales
+    overflow for amaxes past FLT_MAX / 448)."""
+    x_cpu = _bf16_exponent_sweep(M, K)
+    x, ra, ca = check_row_scaled(x_cpu, bounds=(448.0, 256.0), dequant=False, label="exponent sweep")
+    xf = x_cpu.float().numpy()
+    for rw, cw in ((True, False), (False, True)):
+        out = gpu_quantize(x, p.NVFP4_AMAX_LINE, ra, p.NVFP4_AMAX_LINE, ca, 448.0, rowwise=rw, colwise=cw)
+        if rw:
+            q, s = oracle.quantize_rowwise(xf, oracle.MODE_LINE, oracle.amax_rows(xf), 448.0)
+            assert_same("q_row", to_np(out["q_row"]), q)
+            assert_same("s_row", to_np(out["s_row"]), s)
+        if cw:
+            q, s = oracle.quantize_colwise(xf, oracle.MODE_LINE, oracle.amax_cols(xf), 448.0)
+            assert_same("q_col", to_np(out["q_col"]), q)
+            assert_same("s_col", to_np(out["s_col"]), s)
