@@ -180,6 +180,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time the CPU oracle is run for (whole passes)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--hold-ms", type=float, default=100.0,
+                    help="length of the spin kernel queued ahead of each timed region")
     return ap.parse_args()
 
 
@@ -234,6 +236,23 @@ def main():
         p.nvfp4_quantize_transpose(xs[i & 1], p.NVFP4_AMAX_LINE, ra, p.NVFP4_AMAX_LINE, ca, bound,
                                    out["q_row"], out["s_row"], out["q_col"], out["s_col"])
 
+    # A bounded spin kernel at the head of the stream keeps the GPU busy
+    # while the host enqueues a whole timed region, so the region's kernels
+    # run back to back from the queue with no launch gaps, also when a
+    # profiler slows every host-side launch. Its length is calibrated once.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+    e0.record()
+    torch.cuda._sleep(1 << 20)
+    e1.record()
+    torch.cuda.synchronize()
+    sleep_cycles_per_ms = (1 << 20) / max(e0.elapsed_time(e1), 1e-3)
+
+    def hold_queue(ms):
+        torch.cuda._sleep(int(ms * sleep_cycles_per_ms))
+
     def timed(fn, n):
         """Average time of fn(0..n-1) launched back to back, HIP events on the
         launch stream at the two ends of the region only (an event between two
@@ -241,6 +260,7 @@ def main():
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        hold_queue(args.hold_ms)
         e0.record()
         for i in range(n):
             fn(i)
@@ -261,6 +281,7 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K_steps)]
     torch.cuda.synchronize()
+    hold_queue(args.hold_ms)
     for i in range(K_steps):
         amax(i)
         ev[i][0].record()

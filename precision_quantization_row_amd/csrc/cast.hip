@@ -105,10 +105,10 @@ __device__ __forceinline__ float elem_c(const uint32_t (&w)[16][Blk<T>::NW], int
 // DPP quad_perm [0,0,2,2] / [1,1,3,3]: both lanes of a pair get the even /
 // the odd lane's value.
 __device__ __forceinline__ float bcast_even(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xA0, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xA0, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float bcast_odd(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xF5, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xF5, 0xF, 0xF, true));
 }
 
 // ------------------------------------------------------------------ loads
@@ -505,7 +505,7 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
     }
   }
   // the fast forms hold for bamax >= 2^-125 and D in [2^-126, 2^126)
-  const bool ok = (bmin >= 0x01000000u) & (dmin >= 0x00800000u) & (dmax < 0x7E800000u);
+  const bool ok = (bmin >= kFastBamaxMin) & (dmin >= 0x00800000u) & (dmax < 0x7E800000u);
   if (!ok) {
     // The block maxima pass through an empty asm statement so that the
     // compiler cannot share work between the two forms: sharing would keep

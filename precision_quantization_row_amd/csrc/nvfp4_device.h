@@ -99,15 +99,21 @@ __device__ __forceinline__ void block_scale(float bamax, float a, float s_enc, f
 }
 
 // The unguarded scale chain itself: *byte (low byte) and *enc as block_scale
-// gives them whenever bamax >= 2^-125 and D lies in [2^-126, 2^126); returns
+// gives them whenever bamax >= 2^-121 and D lies in [2^-126, 2^126); returns
 // D's bit pattern so that callers can check that range for many blocks at once.
-// The converter keeps the upper half of its first operand's register, so it
-// starts from s32's own bits (no zeroing move); only the low byte is used.
+// RN(bamax / 6) is fma(bamax, H, RN(bamax * L)) with H = RN(1/6) and
+// L = RN(1/6 - H): bamax / 6 is never closer to a rounding midpoint than a
+// sixth of an ulp, far more than this two-term product's error, and the
+// result equals the IEEE quotient for every finite bamax >= 2^-121 (checked
+// exhaustively, binary32 arithmetic emulated exactly). The converter keeps
+// the upper half of its first operand's register, so it starts from s32's
+// own bits (no zeroing move); only the low byte is used.
+constexpr uint32_t kFastBamaxMin = 0x03000000u;  // bit pattern of 2^-121
 __device__ __forceinline__ uint32_t block_scale_unchecked(float bamax, float a, float s_enc,
                                                           float f_inv, uint32_t* byte, float* enc) {
   constexpr float kR6 = 0.16666667163372039794921875f;  // RN(1/6)
-  const float q0 = bamax * kR6;
-  const float q = __builtin_fmaf(__builtin_fmaf(-q0, kE2M1Max, bamax), kR6, q0);
+  constexpr float kR6lo = -0x1.555556p-28f;              // RN(1/6 - RN(1/6))
+  const float q = __builtin_fmaf(bamax, kR6, bamax * kR6lo);
   const float s32 = fminf(q * s_enc, kE4M3Max);
   const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(s32, s32, __float_as_int(s32), false);
   *byte = (uint32_t)pk;
@@ -119,7 +125,7 @@ __device__ __forceinline__ uint32_t block_scale_unchecked(float bamax, float a, 
 }
 
 // block_scale without its range guards, for the batched block code: the same
-// results whenever bamax >= 2^-125 (div6_rn's fast form) and D lies in
+// results whenever bamax >= 2^-121 (the two-term quotient above) and D lies in
 // [2^-126, 2^126) (recip_rn's fast form; then D != 0 too), which it reports.
 // *byte is the converter's packed result: its low byte is the scale byte.
 // Callers redo the lanes where it returns false with block_scale.
@@ -127,7 +133,7 @@ __device__ __forceinline__ bool block_scale_fast(float bamax, float a, float s_e
                                                  uint32_t* byte, float* enc) {
   const uint32_t db = block_scale_unchecked(bamax, a, s_enc, f_inv, byte, enc);
   const uint32_t bb = __float_as_uint(bamax);
-  return (bb >= 0x01000000u) & ((db - 0x00800000u) < 0x7E000000u);
+  return (bb >= kFastBamaxMin) & ((db - 0x00800000u) < 0x7E000000u);
 }
 
 // block_scale that also returns the block's decode scale D (the factor the
