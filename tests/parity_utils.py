@@ -103,3 +103,24 @@ def check_row_scaled(x_cpu: torch.Tensor, bounds=(448.0,), flags=0, dequant=True
                 assert_same(f"dequant col {od} b={bound}", dequant_bits(y),
                             oracle_dequant_bits(qc, sc, K, M, oracle.MODE_LINE, ca_o, bound, od))
     return x, ra, ca
+
+
+def bf16_exponent_sweep(M: int, K: int, seed: int = 11) -> torch.Tensor:
+    """N(0,1) rows scaled by 2^e with e swept over the BF16 range (subnormal
+    rows included), plus planted elements: single magnitudes in [2^121,
+    2^126] inside ordinary rows, a row of exactly 2^121, a row of BF16
+    subnormals and an all-zero row. Magnitudes of 2^121 and above are the
+    patterns that read as f16 infinities or NaNs."""
+    g = torch.Generator().manual_seed(seed)
+    z = torch.randn(M, K, generator=g)
+    e = torch.linspace(-140.0, 124.0, M).round()
+    x = z * torch.pow(2.0, e)[:, None]
+    idx = torch.randperm(M * K, generator=g)[: M * K // 997]
+    x.view(-1)[idx] = torch.pow(2.0, torch.randint(121, 127, (idx.numel(),), generator=g).float()) * \
+        torch.where(torch.rand(idx.numel(), generator=g) < 0.5, -1.0, 1.0)
+    x[M // 3] = 2.0 ** 121
+    x[M // 2] = torch.where(torch.rand(K, generator=g) < 0.5, -1.0, 1.0) * 2.0 ** -130
+    x[M // 5] = 0.0
+    xb = x.to(torch.bfloat16)
+    assert torch.isfinite(xb.float()).all()
+    return xb

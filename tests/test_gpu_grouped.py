@@ -15,7 +15,7 @@ import oracle
 import precision_quantization_row_amd as p
 from precision_quantization_row_amd import workloads
 
-from parity_utils import assert_same, f32_bits, say, to_np
+from parity_utils import assert_same, bf16_exponent_sweep, f32_bits, say, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -250,3 +250,12 @@ def test_full_size_grouped_workload():
     qc, scc = oracle.quantize_colwise(xc, oracle.MODE_ROWGROUP, ra.cpu().numpy(), 448.0)
     assert_same("q_col[sampled]", to_np(out["q_col"][cols]), qc)
     assert_same("s_col[sampled]", to_np(out["s_col"][cols]), scc)
+
+
+def test_grouped_bf16_whole_exponent_range():
+    """Token rows with BF16 magnitudes from subnormal to 2^126 (the patterns
+    that read as f16 infinities or NaNs included) through the grouped
+    macro-tile kernel, byte for byte against the oracle."""
+    x = bf16_exponent_sweep(427, 512, seed=12)
+    group_rows = [200, 77, 0, 150]
+    _check("exponent sweep", x, group_rows, 128, _full_rows(group_rows, 128))

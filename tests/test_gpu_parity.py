@@ -10,8 +10,9 @@ import oracle
 import precision_quantization_row_amd as p
 from precision_quantization_row_amd import workloads
 
-from parity_utils import (assert_same, check_row_scaled, dequant_bits, f32_bits, gpu_amax,
-                          gpu_dequant, gpu_quantize, oracle_dequant_bits, say, to_np)
+from parity_utils import (assert_same, bf16_exponent_sweep, check_row_scaled, dequant_bits,
+                          f32_bits, gpu_amax, gpu_dequant, gpu_quantize, oracle_dequant_bits, say,
+                          to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -286,34 +287,13 @@ def test_interior_with_columns_past_the_last_strip(dtype, M, K):
 
 
 # ------------------------------------- BF16 magnitudes over the whole range
-def _bf16_exponent_sweep(M: int, K: int, seed: int = 11) -> torch.Tensor:
-    """N(0,1) rows scaled by 2^e with e swept over the BF16 range (subnormal
-    rows included), plus planted elements: single magnitudes in [2^121,
-    2^126] inside ordinary rows, a row of exactly 2^121, a row of BF16
-    subnormals and an all-zero row. Magnitudes of 2^121 and above are the
-    patterns that read as f16 infinities or NaNs."""
-    g = torch.Generator().manual_seed(seed)
-    z = torch.randn(M, K, generator=g)
-    e = torch.linspace(-140.0, 124.0, M).round()
-    x = z * torch.pow(2.0, e)[:, None]
-    idx = torch.randperm(M * K, generator=g)[: M * K // 997]
-    x.view(-1)[idx] = torch.pow(2.0, torch.randint(121, 127, (idx.numel(),), generator=g).float()) * \
-        torch.where(torch.rand(idx.numel(), generator=g) < 0.5, -1.0, 1.0)
-    x[M // 3] = 2.0 ** 121
-    x[M // 2] = torch.where(torch.rand(K, generator=g) < 0.5, -1.0, 1.0) * 2.0 ** -130
-    x[M // 5] = 0.0
-    xb = x.to(torch.bfloat16)
-    assert torch.isfinite(xb.float()).all()
-    return xb
-
-
 @pytest.mark.parametrize("M,K", [(512, 512), (256, 768)])
 def test_bf16_whole_exponent_range(M, K):
     """Every output byte against the oracle for BF16 magnitudes from
     subnormal to 2^126, through the macro-tile kernel: both directions and
     each alone, bounds 448 and 256 (dequantize is left out: decode scales
     overflow for amaxes past FLT_MAX / 448)."""
-    x_cpu = _bf16_exponent_sweep(M, K)
+    x_cpu = bf16_exponent_sweep(M, K)
     x, ra, ca = check_row_scaled(x_cpu, bounds=(448.0, 256.0), dequant=False, label="exponent sweep")
     xf = x_cpu.float().numpy()
     for rw, cw in ((True, False), (False, True)):
