@@ -163,6 +163,57 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
     res["moe_%dtok_x%d_quantize_grouped" % (T, K)] = _row(
         timed(grouped, n) * 1e3, gb, "token rows read by the amax and the cast, padded layout written")
     del tok, out
+
+    # the two small matrices, one whole quantize each (amax pass + cast),
+    # cold: a 512 MB fill evicts the memory-side cache before every rep, and
+    # the median of the reps is reported (the 256 x 256 case is launch-bound)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def cold(fn, reps=20):
+        fn()
+        ts = []
+        for i in range(reps):
+            flush.fill_(i & 0xFF)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return 0.5 * (ts[(reps - 1) // 2] + ts[reps // 2])
+
+    for name in ("tiny_rowscale", "outliers"):
+        w = workloads.make(name)
+        M, K = w.shape
+        x = w.x.to(dev)
+        ra = torch.empty(M, dtype=torch.float32, device=dev)
+        ca = torch.empty(K, dtype=torch.float32, device=dev)
+        ta = torch.empty(1, dtype=torch.float32, device=dev)
+        out = p.empty_outputs(M, K, dev)
+
+        def row_scaled():
+            p.nvfp4_amax_rowcol(x, ra, ca)
+            p.nvfp4_quantize_transpose(x, 1, ra, 1, ca, bound, out["q_row"], out["s_row"],
+                                       out["q_col"], out["s_col"])
+
+        def per_tensor():
+            p.nvfp4_amax_rowcol(x, None, None, tensor_amax=ta)
+            p.nvfp4_quantize_transpose(x, 0, ta, 0, ta, bound, out["q_row"], out["s_row"],
+                                       out["q_col"], out["s_col"])
+
+        res["%s_%dx%d_row_scaled_cold" % (name, M, K)] = _row(
+            cold(row_scaled) * 1e3, workloads.algorithmic_bytes(M, K, 2),
+            "X read by the amax and the cast passes, both copies written; median of 20 cold reps")
+        if name == "outliers":
+            res["%s_%dx%d_per_tensor_cold" % (name, M, K)] = _row(
+                cold(per_tensor) * 1e3,
+                workloads.algorithmic_bytes(M, K, 2, row_amax=False, col_amax=False,
+                                            tensor_amax=True),
+                "X read by the amax and the cast passes, both copies written; median of 20 cold reps")
+        del x, out
+    del flush
     return res
 
 

@@ -301,12 +301,16 @@ __global__ void __launch_bounds__(256) col_amax_kernel(const T* __restrict__ x, 
 }
 
 // ------------------------------------------------------------ tensor amax
+// A persistent grid of at most one 16-wave workgroup per CU: each wave keeps
+// four 1 KB loads in flight, and only one atomic per workgroup reaches the
+// result word (same-word atomics from thousands of workgroups serialize).
+constexpr int TENSOR_THREADS = 1024;
 template <typename T, bool VEC>
-__global__ void __launch_bounds__(256) tensor_amax_kernel(const T* __restrict__ x, int64_t n,
+__global__ void __launch_bounds__(TENSOR_THREADS) tensor_amax_kernel(const T* __restrict__ x, int64_t n,
                                                           float* __restrict__ ta,
                                                           const float* noop) {
   if (skip(noop)) return;
-  __shared__ uint32_t red[4];
+  __shared__ uint32_t red[TENSOR_THREADS / 64];
   constexpr int V = 16 / sizeof(T);
   const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -338,7 +342,9 @@ __global__ void __launch_bounds__(256) tensor_amax_kernel(const T* __restrict__ 
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t v = max(max(red[0], red[1]), max(red[2], red[3]));
+    uint32_t v = 0u;
+#pragma unroll
+    for (int r = 0; r < TENSOR_THREADS / 64; ++r) v = max(v, red[r]);
     atomicMax(reinterpret_cast<unsigned int*>(ta), v);
   }
 }
@@ -513,11 +519,16 @@ static int launch_tensor_t(const void* xv, int64_t n, float* ta, const float* no
   const T* x = static_cast<const T*>(xv);
   const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   constexpr int V = 16 / sizeof(T);
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n / V + 255) / 256, (int64_t)num_cus() * 8));
+  // one workgroup of 16 waves per CU at most: every workgroup ends with an
+  // atomic on the same word, and those queue behind each other
+  const int64_t blocks = std::max<int64_t>(
+      1, std::min<int64_t>((n / V + 4 * TENSOR_THREADS - 1) / (4 * TENSOR_THREADS), (int64_t)num_cus()));
   if (vec)
-    hipLaunchKernelGGL((tensor_amax_kernel<T, true>), dim3((unsigned)blocks), dim3(256), 0, s, x, n, ta, noop);
+    hipLaunchKernelGGL((tensor_amax_kernel<T, true>), dim3((unsigned)blocks), dim3(TENSOR_THREADS), 0, s,
+                       x, n, ta, noop);
   else
-    hipLaunchKernelGGL((tensor_amax_kernel<T, false>), dim3((unsigned)blocks), dim3(256), 0, s, x, n, ta, noop);
+    hipLaunchKernelGGL((tensor_amax_kernel<T, false>), dim3((unsigned)blocks), dim3(TENSOR_THREADS), 0, s,
+                       x, n, ta, noop);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
