@@ -3,6 +3,7 @@
 // Validation happens before anything is enqueued; the host never reads device
 // memory (noop, amax and group offsets stay on the device), so every call is
 // asynchronous on the caller's stream. The library owns no device memory.
+#include <atomic>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -13,14 +14,19 @@
 namespace nvfp4 {
 
 int num_cus() {
-  static int cache[64] = {0};
+  // per-device cache; calls from several host threads may fill an entry
+  // concurrently (with the same value), hence the atomics
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     n = 256;
-  if (dev < 64) cache[dev] = n;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
