@@ -55,6 +55,9 @@ def _load():
         "orc_quantize_line": (None, [f32p, i64, i64, f32p, c_f, u8p, u8p]),
         "orc_quantize_rowwise": (None, [f32p, i64, i64, c_int, f32p, c_f, u8p, u8p]),
         "orc_quantize_colwise": (None, [f32p, i64, i64, c_int, f32p, c_f, u8p, u8p]),
+        "orc_quantize_line_46": (None, [f32p, i64, i64, f32p, c_f, u8p, u8p]),
+        "orc_quantize_rowwise_46": (None, [f32p, i64, i64, c_int, f32p, c_f, u8p, u8p]),
+        "orc_quantize_colwise_46": (None, [f32p, i64, i64, c_int, f32p, c_f, u8p, u8p]),
         "orc_dequantize": (None, [u8p, u8p, i64, i64, c_int, f32p, c_f, f32p]),
         "orc_quantize_2d": (None, [f32p, i64, i64, c_f, c_f, u8p, u8p, u8p, u8p]),
         "orc_amax_rows": (None, [f32p, i64, i64, f32p]),
@@ -187,6 +190,47 @@ def quantize_colwise(X, mode: int, amax, bound: float = 448.0):
     s = np.zeros((K, (M + 15) // 16), dtype=np.uint8)
     _load().orc_quantize_colwise(_p(X, ctypes.c_float), M, K, mode, _p(a, ctypes.c_float),
                                  float(bound), _p(q, ctypes.c_uint8), _p(s, ctypes.c_uint8))
+    return q, s
+
+
+def quantize_rowwise_46(X, mode: int, amax, bound: float = 256.0):
+    """quantize_rowwise with four-over-six block scales: per block, the scale
+    that maps the block max to 6 or the one that maps it to 4, whichever
+    dequantizes with the smaller squared error (see the C file)."""
+    X = _f32(X)
+    M, K = X.shape
+    a = _amax_arg(mode, amax, M, K)
+    q = np.zeros((M, (K + 1) // 2), dtype=np.uint8)
+    s = np.zeros((M, (K + 15) // 16), dtype=np.uint8)
+    _load().orc_quantize_rowwise_46(_p(X, ctypes.c_float), M, K, mode, _p(a, ctypes.c_float),
+                                    float(bound), _p(q, ctypes.c_uint8), _p(s, ctypes.c_uint8))
+    return q, s
+
+
+def quantize_colwise_46(X, mode: int, amax, bound: float = 256.0):
+    """quantize_colwise with four-over-six block scales."""
+    X = _f32(X)
+    M, K = X.shape
+    a = _amax_arg(mode, amax, K, M)
+    q = np.zeros((K, (M + 1) // 2), dtype=np.uint8)
+    s = np.zeros((K, (M + 15) // 16), dtype=np.uint8)
+    _load().orc_quantize_colwise_46(_p(X, ctypes.c_float), M, K, mode, _p(a, ctypes.c_float),
+                                    float(bound), _p(q, ctypes.c_uint8), _p(s, ctypes.c_uint8))
+    return q, s
+
+
+def quantize_line_46(x, block_amax, bound: float = 256.0):
+    """One line with four-over-six block scales and an explicit second-level
+    amax per 16-element block."""
+    x = _f32(x).ravel()
+    n = x.size
+    ba = np.ascontiguousarray(block_amax, dtype=np.float32).ravel()
+    if ba.size != (n + 15) // 16:
+        raise ValueError("one amax per block is required")
+    q = np.zeros((n + 1) // 2, dtype=np.uint8)
+    s = np.zeros((n + 15) // 16, dtype=np.uint8)
+    _load().orc_quantize_line_46(_p(x, ctypes.c_float), n, 1, _p(ba, ctypes.c_float), float(bound),
+                                 _p(q, ctypes.c_uint8), _p(s, ctypes.c_uint8))
     return q, s
 
 

@@ -153,10 +153,10 @@ float orc_global_encode_scale(float a, float bound) {
  * ------------------------------------------------------------------------- */
 /* The scale byte and the encode factor of a block whose max magnitude is
  * bamax, under second-level amax a (the steps s32 .. enc above). */
-static float block_scale(float bamax, float a, float bound, uint8_t *scale_byte) {
+static float block_scale_to(float bamax, float top, float a, float bound, uint8_t *scale_byte) {
   const float s_enc = orc_global_encode_scale(a, bound);
   const float f_inv = orc_factor_inv(bound);
-  float s32 = (bamax / 6.0f) * s_enc;
+  float s32 = (bamax / top) * s_enc;
   if (s32 > 448.0f) s32 = 448.0f;
   uint8_t b = orc_e4m3_encode(s32);
   float sq = orc_e4m3_value(b);
@@ -168,6 +168,15 @@ static float block_scale(float bamax, float a, float bound, uint8_t *scale_byte)
   }
   *scale_byte = b;
   return enc;
+}
+
+static float block_scale(float bamax, float a, float bound, uint8_t *scale_byte) {
+  return block_scale_to(bamax, 6.0f, a, bound, scale_byte);
+}
+
+/* The FP32 decode scale of a stored byte (the [P4] expression). */
+static float decode_scale(uint8_t byte, float a, float bound) {
+  return (orc_e4m3_value(byte) * a) * orc_factor_inv(bound);
 }
 
 static void quantize_block(const float *x, int64_t stride, int n, float a,
@@ -183,20 +192,77 @@ static void quantize_block(const float *x, int64_t stride, int n, float a,
   for (int k = 0; k < n; ++k) codes[k] = orc_e2m1_encode(x[(int64_t)k * stride] * enc);
 }
 
+/* ---------------------------------------------------------------------------
+ * Four-over-six block scaling ([P3] and [P4] descriptions: the recipe's
+ * "four-over-six" quantizer with an MSE choice and the bound-256 second-level
+ * scale; the pages name the method and define nothing more). Reading: a block
+ * has two candidate scales, the standard one (block max mapped to the largest
+ * E2M1 magnitude, 6) and one that maps the block max to 4:
+ *   s32 = RN( RN(bamax / 6) * S_enc )   or   RN( RN(bamax / 4) * S_enc ),
+ * each through the same byte / D / enc / code steps as above. Each candidate
+ * is dequantized as the decoder does it, y_k = RN(e2m1(code_k) * D), and the
+ * one with the smaller squared error is kept (the standard one on a tie).
+ * The error is taken in binary64: d_k = (double)x_k - (double)y_k, the
+ * rounded square d_k * d_k, the squares of elements 0..7 summed in order, of
+ * elements 8..15 summed in order, then the two sums added (a short last block
+ * uses the elements it has, split the same way). The kept byte decodes
+ * through the same expression, so the dequantizer needs no flag.
+ * ------------------------------------------------------------------------- */
+static double block_sq_error(const float *x, int64_t stride, int n, const uint8_t *codes,
+                             float d) {
+  double lo = 0.0, hi = 0.0;
+  for (int k = 0; k < n; ++k) {
+    const float y = orc_e2m1_value(codes[k]) * d;
+    const double e = (double)x[(int64_t)k * stride] - (double)y;
+    const double e2 = e * e;
+    if (k < 8)
+      lo = lo + e2;
+    else
+      hi = hi + e2;
+  }
+  return lo + hi;
+}
+
+static void quantize_block_46(const float *x, int64_t stride, int n, float a, float bound,
+                              uint8_t *codes, uint8_t *scale_byte) {
+  float bamax = 0.0f;
+  for (int k = 0; k < n; ++k) {
+    float v = x[(int64_t)k * stride];
+    assert(isfinite(v));
+    float m = fabsf(v);
+    if (m > bamax) bamax = m;
+  }
+  uint8_t b6, b4, c6[16], c4[16];
+  const float enc6 = block_scale_to(bamax, 6.0f, a, bound, &b6);
+  const float enc4 = block_scale_to(bamax, 4.0f, a, bound, &b4);
+  for (int k = 0; k < n; ++k) {
+    c6[k] = orc_e2m1_encode(x[(int64_t)k * stride] * enc6);
+    c4[k] = orc_e2m1_encode(x[(int64_t)k * stride] * enc4);
+  }
+  const double e6 = block_sq_error(x, stride, n, c6, decode_scale(b6, a, bound));
+  const double e4 = block_sq_error(x, stride, n, c4, decode_scale(b4, a, bound));
+  const int four = e4 < e6;
+  *scale_byte = four ? b4 : b6;
+  memcpy(codes, four ? c4 : c6, (size_t)n);
+}
+
 /* Quantize one line of n elements (element k at x[k*stride]).
  * block_amax[b] is the second-level amax block b uses.
  * Output: ceil(n/2) packed code bytes -- element 2t in the low nibble, 2t+1
  * in the high nibble, a missing last high nibble is 0 (reading; [P3] only says
  * the two nibble lanes exist) -- and ceil(n/16) scale bytes. */
-void orc_quantize_line(const float *x, int64_t n, int64_t stride,
-                       const float *block_amax, float bound, uint8_t *q,
-                       uint8_t *s) {
+static void quantize_line_impl(const float *x, int64_t n, int64_t stride,
+                               const float *block_amax, float bound, int four_six,
+                               uint8_t *q, uint8_t *s) {
   const int64_t nblk = (n + 15) / 16;
   memset(q, 0, (size_t)((n + 1) / 2));
   for (int64_t b = 0; b < nblk; ++b) {
     int cnt = (int)((n - 16 * b) < 16 ? (n - 16 * b) : 16);
     uint8_t codes[16];
-    quantize_block(x + 16 * b * stride, stride, cnt, block_amax[b], bound, codes, &s[b]);
+    if (four_six)
+      quantize_block_46(x + 16 * b * stride, stride, cnt, block_amax[b], bound, codes, &s[b]);
+    else
+      quantize_block(x + 16 * b * stride, stride, cnt, block_amax[b], bound, codes, &s[b]);
     for (int k = 0; k < cnt; ++k) {
       int64_t e = 16 * b + k;
       if (e & 1)
@@ -205,6 +271,18 @@ void orc_quantize_line(const float *x, int64_t n, int64_t stride,
         q[e >> 1] |= codes[k];
     }
   }
+}
+
+void orc_quantize_line(const float *x, int64_t n, int64_t stride,
+                       const float *block_amax, float bound, uint8_t *q,
+                       uint8_t *s) {
+  quantize_line_impl(x, n, stride, block_amax, bound, 0, q, s);
+}
+
+void orc_quantize_line_46(const float *x, int64_t n, int64_t stride,
+                          const float *block_amax, float bound, uint8_t *q,
+                          uint8_t *s) {
+  quantize_line_impl(x, n, stride, block_amax, bound, 1, q, s);
 }
 
 /* The second-level amax of block b of a line, by mode. */
@@ -218,33 +296,55 @@ static float block_amax_of(int mode, const float *amax, int64_t line, int64_t b)
 
 /* Rowwise copy: line i = row i of X [M][K] (K-contiguous) -> q [M][ceil(K/2)],
  * s [M][ceil(K/16)]. ([P1] sequence diagram: rowwise FP4 feeds fprop.) */
-void orc_quantize_rowwise(const float *X, int64_t M, int64_t K, int mode,
-                          const float *amax, float bound, uint8_t *q, uint8_t *s) {
+static void quantize_rows_impl(const float *X, int64_t M, int64_t K, int mode,
+                               const float *amax, float bound, int four_six, uint8_t *q,
+                               uint8_t *s) {
   const int64_t qb = (K + 1) / 2, sb = (K + 15) / 16;
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t i = 0; i < M; ++i) {
     float *ba = (float *)malloc((size_t)sb * sizeof(float));
     assert(ba);
     for (int64_t b = 0; b < sb; ++b) ba[b] = block_amax_of(mode, amax, i, b);
-    orc_quantize_line(X + i * K, K, 1, ba, bound, q + i * qb, s + i * sb);
+    quantize_line_impl(X + i * K, K, 1, ba, bound, four_six, q + i * qb, s + i * sb);
     free(ba);
   }
+}
+
+void orc_quantize_rowwise(const float *X, int64_t M, int64_t K, int mode,
+                          const float *amax, float bound, uint8_t *q, uint8_t *s) {
+  quantize_rows_impl(X, M, K, mode, amax, bound, 0, q, s);
+}
+
+void orc_quantize_rowwise_46(const float *X, int64_t M, int64_t K, int mode,
+                             const float *amax, float bound, uint8_t *q, uint8_t *s) {
+  quantize_rows_impl(X, M, K, mode, amax, bound, 1, q, s);
 }
 
 /* Columnwise (transposed) copy: line j = column j of X -> q [K][ceil(M/2)],
  * s [K][ceil(M/16)]. ([P1] summary: the columnwise output is the transpose,
  * consumed by wgrad; its per-column amax has K entries.) */
-void orc_quantize_colwise(const float *X, int64_t M, int64_t K, int mode,
-                          const float *amax, float bound, uint8_t *q, uint8_t *s) {
+static void quantize_cols_impl(const float *X, int64_t M, int64_t K, int mode,
+                               const float *amax, float bound, int four_six, uint8_t *q,
+                               uint8_t *s) {
   const int64_t qb = (M + 1) / 2, sb = (M + 15) / 16;
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t j = 0; j < K; ++j) {
     float *ba = (float *)malloc((size_t)sb * sizeof(float));
     assert(ba);
     for (int64_t b = 0; b < sb; ++b) ba[b] = block_amax_of(mode, amax, j, b);
-    orc_quantize_line(X + j, M, K, ba, bound, q + j * qb, s + j * sb);
+    quantize_line_impl(X + j, M, K, ba, bound, four_six, q + j * qb, s + j * sb);
     free(ba);
   }
+}
+
+void orc_quantize_colwise(const float *X, int64_t M, int64_t K, int mode,
+                          const float *amax, float bound, uint8_t *q, uint8_t *s) {
+  quantize_cols_impl(X, M, K, mode, amax, bound, 0, q, s);
+}
+
+void orc_quantize_colwise_46(const float *X, int64_t M, int64_t K, int mode,
+                             const float *amax, float bound, uint8_t *q, uint8_t *s) {
+  quantize_cols_impl(X, M, K, mode, amax, bound, 1, q, s);
 }
 
 /* ---------------------------------------------------------------------------
