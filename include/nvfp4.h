@@ -130,6 +130,24 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
                              float bound, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
                              uint8_t* s_col, const float* noop, void* stream);
 
+/* Four-over-six block scales (four-over-six grouped-GEMM and backward-
+ * overrides PR descriptions: the quantizer is named there together with its
+ * MSE choice and its bound-256 second-level scale; nothing more is defined,
+ * so this is a reading). Arguments, layouts, modes, validation and noop are
+ * those of nvfp4_quantize_transpose. Each 1x16 block gets one of two scales:
+ * the standard one (block max mapped to the E2M1 maximum 6) or the one that
+ * maps the block max to 4, whichever dequantizes the block with the smaller
+ * squared error (summed in binary64: elements 0..7 in order, elements 8..15
+ * in order, then the two sums; the max-6 scale on a tie). The chosen byte is
+ * an ordinary E4M3 block scale, so nvfp4_dequantize decodes the result
+ * unchanged. Bound 256 keeps the max-4 scale of a block that holds the line
+ * amax below 448 (6/4 * 256 = 384). Runs on the checked kernel over the
+ * whole matrix (it computes both candidates per block). */
+int nvfp4_quantize_4over6(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
+                          const float* row_amax, int col_mode, const float* col_amax, float bound,
+                          uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                          const float* noop, void* stream);
+
 /* 2-D 16 x 16 blocks (backward-overrides PR description: its 1x16 weight
  * option mirrors TE's switch that turns 2-D weight quantization off, so 2-D
  * blocks are TE's default for weights; the pages define nothing more). One

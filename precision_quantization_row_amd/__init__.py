@@ -39,7 +39,8 @@ NVFP4_FLAG_FORCE_TWO_KERNEL = 1
 
 # Every entry point include/nvfp4.h declares.
 EXPORTED = ("nvfp4_amax_path", "nvfp4_amax_rowcol", "nvfp4_group_amax_expand",
-            "nvfp4_quantize_transpose", "nvfp4_quantize_2d", "nvfp4_quantize_grouped",
+            "nvfp4_quantize_transpose", "nvfp4_quantize_4over6", "nvfp4_quantize_2d",
+            "nvfp4_quantize_grouped",
             "nvfp4_quantize_dequantize", "nvfp4_dequantize",
             "nvfp4_status_string")
 
@@ -77,6 +78,9 @@ def load_library():
     lib.nvfp4_quantize_transpose.restype = c_int
     lib.nvfp4_quantize_transpose.argtypes = [vp, c_int, i64, i64, c_int, f32p, c_int, f32p, c_f,
                                              u8p, u8p, u8p, u8p, f32p, vp]
+    lib.nvfp4_quantize_4over6.restype = c_int
+    lib.nvfp4_quantize_4over6.argtypes = [vp, c_int, i64, i64, c_int, f32p, c_int, f32p, c_f,
+                                          u8p, u8p, u8p, u8p, f32p, vp]
     lib.nvfp4_quantize_2d.restype = c_int
     lib.nvfp4_quantize_2d.argtypes = [vp, c_int, i64, i64, f32p, c_f, u8p, u8p, u8p, u8p, f32p, vp]
     lib.nvfp4_quantize_grouped.restype = c_int
@@ -193,6 +197,22 @@ def nvfp4_quantize_transpose(x: torch.Tensor, row_mode: int, row_amax: Optional[
                              q_row: Optional[torch.Tensor], s_row: Optional[torch.Tensor],
                              q_col: Optional[torch.Tensor], s_col: Optional[torch.Tensor],
                              noop: Optional[torch.Tensor] = None, stream=None) -> None:
+    _quantize("nvfp4_quantize_transpose", x, row_mode, row_amax, col_mode, col_amax, bound,
+              q_row, s_row, q_col, s_col, noop, stream)
+
+
+def nvfp4_quantize_4over6(x: torch.Tensor, row_mode: int, row_amax: Optional[torch.Tensor],
+                          col_mode: int, col_amax: Optional[torch.Tensor], bound: float,
+                          q_row: Optional[torch.Tensor], s_row: Optional[torch.Tensor],
+                          q_col: Optional[torch.Tensor], s_col: Optional[torch.Tensor],
+                          noop: Optional[torch.Tensor] = None, stream=None) -> None:
+    """nvfp4_quantize_transpose with four-over-six block scales."""
+    _quantize("nvfp4_quantize_4over6", x, row_mode, row_amax, col_mode, col_amax, bound,
+              q_row, s_row, q_col, s_col, noop, stream)
+
+
+def _quantize(name, x, row_mode, row_amax, col_mode, col_amax, bound, q_row, s_row, q_col, s_col,
+              noop, stream) -> None:
     lib = load_library()
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
@@ -209,11 +229,10 @@ def nvfp4_quantize_transpose(x: torch.Tensor, row_mode: int, row_amax: Optional[
         _dev(q_col, "q_col", (torch.uint8,), K * ((M + 1) // 2), dev)
         _dev(s_col, "s_col", _SCALE_DTYPES, K * ((M + 15) // 16), dev)
     _dev(noop, "noop", _F32, 1, dev)
-    st = lib.nvfp4_quantize_transpose(_ptr(x), _dtype_code(x), M, K, row_mode, _ptr(row_amax),
-                                      col_mode, _ptr(col_amax), ctypes.c_float(bound),
-                                      _ptr(q_row), _ptr(s_row), _ptr(q_col), _ptr(s_col),
-                                      _ptr(noop), _stream(stream, dev))
-    _check("nvfp4_quantize_transpose", st)
+    st = getattr(lib, name)(_ptr(x), _dtype_code(x), M, K, row_mode, _ptr(row_amax), col_mode,
+                            _ptr(col_amax), ctypes.c_float(bound), _ptr(q_row), _ptr(s_row),
+                            _ptr(q_col), _ptr(s_col), _ptr(noop), _stream(stream, dev))
+    _check(name, st)
 
 
 def nvfp4_quantize_2d(x: torch.Tensor, tensor_amax: torch.Tensor, bound: float,

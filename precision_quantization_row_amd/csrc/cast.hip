@@ -67,6 +67,8 @@ struct CastK {
   int64_t grp_G, grp_align, grp_T;
   // 2-D blocks: one scale per 16 x 16 tile, per-tensor amax row_amax[0]
   int blk2d;
+  // four-over-six block scales (1x16 blocks; the checked kernel only)
+  int four_six;
 };
 
 // Lane block storage: NW dwords per row. BF16: 4 dwords = 8 values (element
@@ -330,6 +332,147 @@ __device__ __forceinline__ void process_block(const uint32_t (&w)[16][Blk<T>::NW
                                      elem_c<T>(w, 12, k) * enc, elem_c<T>(w, 13, k) * enc,
                                      elem_c<T>(w, 14, k) * enc, elem_c<T>(w, 15, k) * enc);
       st.col(k, w0, w1, byte);
+    }
+  }
+}
+
+// ------------------------------------------------------- four-over-six
+// Four-over-six block scaling (the torchao four-over-six PR descriptions name
+// the quantizer, its MSE choice and its bound-256 second-level scale). Each
+// block has two candidate scales, the block max mapped to the E2M1 maximum 6
+// or to 4; both go through the same byte / D / encode steps, both candidates
+// are dequantized as the decoder does it (y = RN(e2m1(code) * D)), and the one
+// with the smaller squared error is kept, the max-6 one on a tie. The error is
+// summed in binary64 in a fixed order -- elements 0..7 in order, elements
+// 8..15 in order, then the two sums added -- so every lane that takes a
+// block's decision takes the same one. Blocks cut at the matrix edge read
+// zeros past it, whose squared error is exactly zero.
+struct Cand {
+  uint32_t byte;
+  float enc, dec;
+};
+
+// One candidate: s32 = RN(RN(bamax / top) * S_enc), then the guarded chain
+// (IEEE divisions, no range conditions).
+__device__ __forceinline__ Cand cand_scale(float bamax, float top, float a, float s_enc,
+                                           float f_inv) {
+  const float s32 = fminf((bamax / top) * s_enc, kE4M3Max);
+  const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(s32, s32, 0, false);
+  Cand c;
+  c.byte = (uint32_t)pk & 0xFFu;
+  const float sq = __builtin_amdgcn_cvt_f32_fp8(pk, 0);
+  c.dec = (sq * a) * f_inv;
+  c.enc = (c.dec == 0.0f) ? 0.0f : fminf(1.0f / c.dec, kFltMax);
+  return c;
+}
+
+// Sum over 8 elements, in order, of (x_k - RN(e2m1(code_k) * d))^2 in
+// binary64; code k is nibble k of word (v_cvt_scalef32_pk_f32_fp4 with scale
+// 1.0 decodes it exactly).
+__device__ __forceinline__ double sq_error8(const float (&x)[8], uint32_t word, float d) {
+  float v[8];
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
+  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+  v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+  v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const double e = (double)x[k] - (double)(v[k] * d);
+    s = s + e * e;
+  }
+  return s;
+}
+
+__device__ __forceinline__ double dpp_swap1_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = dpp_swap1((uint32_t)b), hi = dpp_swap1((uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Both directions of one 64-row step with four-over-six block scales (the
+// checked kernel's lane layout: lane pair (l, l ^ 1) holds a row block, the
+// even lane its elements 0..7).
+template <typename T, bool ROWW, bool COLW, class Store, class RowTab, class ColTab>
+__device__ __forceinline__ void process_block_46(const uint32_t (&w)[16][Blk<T>::NW],
+                                                 const Store& st, int g, int par,
+                                                 const RowTab& row, const ColTab& col,
+                                                 float f_inv) {
+  uint32_t cm[8];  // magnitude bits of the lane's column maxima
+#pragma unroll
+  for (int k = 0; k < 8; ++k) cm[k] = 0u;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t h[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * j + e;
+      uint32_t m = 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t av = __float_as_uint(elem<T>(w, i, k)) & kAbsF32;
+        if constexpr (COLW) cm[k] = max(cm[k], av);
+        m = max(m, av);
+      }
+      h[e] = m;
+    }
+    if constexpr (ROWW) {
+      const uint32_t b0 = max(h[0], dpp_swap1(h[0]));
+      const uint32_t b1 = max(h[1], dpp_swap1(h[1]));
+      const int lr = 16 * g + 2 * j + par;
+      const float a = row.a(lr), se = row.s(lr);
+      const float bm = __uint_as_float(par ? b1 : b0);
+      const Cand c6 = cand_scale(bm, kE2M1Max, a, se, f_inv);
+      const Cand c4 = cand_scale(bm, 4.0f, a, se, f_inv);
+      bool four[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        // the candidates of row 2j + e, from the lane that owns it
+        const float e6 = e ? bcast_odd(c6.enc) : bcast_even(c6.enc);
+        const float d6 = e ? bcast_odd(c6.dec) : bcast_even(c6.dec);
+        const float e4 = e ? bcast_odd(c4.enc) : bcast_even(c4.enc);
+        const float d4 = e ? bcast_odd(c4.dec) : bcast_even(c4.dec);
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = elem<T>(w, 2 * j + e, k);
+        const uint32_t w6 = e2m1_pack8(x[0] * e6, x[1] * e6, x[2] * e6, x[3] * e6, x[4] * e6,
+                                       x[5] * e6, x[6] * e6, x[7] * e6);
+        const uint32_t w4 = e2m1_pack8(x[0] * e4, x[1] * e4, x[2] * e4, x[3] * e4, x[4] * e4,
+                                       x[5] * e4, x[6] * e4, x[7] * e4);
+        const double p6 = sq_error8(x, w6, d6), p4 = sq_error8(x, w4, d4);
+        const double q6 = dpp_swap1_f64(p6), q4 = dpp_swap1_f64(p4);
+        const double s6 = par ? q6 + p6 : p6 + q6;  // elements 0..7 first
+        const double s4 = par ? q4 + p4 : p4 + q4;
+        four[e] = s4 < s6;
+        st.row_codes(2 * j + e, four[e] ? w4 : w6);
+      }
+      st.row_scale(j, four[par] ? c4.byte : c6.byte);
+    }
+  }
+  if constexpr (COLW) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t cb = cm[k];
+      const Cand c6 = cand_scale(__uint_as_float(cb), kE2M1Max, col.a(k), col.s(k), f_inv);
+      const Cand c4 = cand_scale(__uint_as_float(cb), 4.0f, col.a(k), col.s(k), f_inv);
+      float lo[8], hi[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = elem<T>(w, i, k);
+        hi[i] = elem<T>(w, 8 + i, k);
+      }
+      auto pack = [](const float (&v)[8], float f) {
+        return e2m1_pack8(v[0] * f, v[1] * f, v[2] * f, v[3] * f, v[4] * f, v[5] * f, v[6] * f,
+                          v[7] * f);
+      };
+      const uint32_t a6 = pack(lo, c6.enc), b6 = pack(hi, c6.enc);
+      const uint32_t a4 = pack(lo, c4.enc), b4 = pack(hi, c4.enc);
+      const double s6 = sq_error8(lo, a6, c6.dec) + sq_error8(hi, b6, c6.dec);
+      const double s4 = sq_error8(lo, a4, c4.dec) + sq_error8(hi, b4, c4.dec);
+      const bool four = s4 < s6;
+      st.col(k, four ? a4 : a6, four ? b4 : b6, four ? c4.byte : c6.byte);
     }
   }
 }
@@ -1074,8 +1217,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
 // workgroup per segment of rows_per_wg rows of one strip, checked loads and
 // stores. Launched over a rectangle: segment seg0 + b / nstrips of the row
 // range [rstart, rend), strip strip0 + b % nstrips.
-template <typename T, bool ROWW, bool COLW, bool B2D>
+template <typename T, bool ROWW, bool COLW, bool B2D, bool FOS = false>
 __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
+  static_assert(!(B2D && FOS), "one block rule at a time");
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   constexpr int NW = Blk<T>::NW;
   __shared__ float row_a_s[CAST_MAX_ROWS_PER_WG];
@@ -1170,7 +1314,10 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
       }
     }
     const LdsTab rows{row_a_s, row_se_s, (int)(r0 - rs)};
-    process_block<T, ROWW, COLW>(w, st, g, par, rows, ColRegs{acol, scol}, p.F_inv);
+    if constexpr (FOS)
+      process_block_46<T, ROWW, COLW>(w, st, g, par, rows, ColRegs{acol, scol}, p.F_inv);
+    else
+      process_block<T, ROWW, COLW>(w, st, g, par, rows, ColRegs{acol, scol}, p.F_inv);
   }
 }
 
@@ -1234,7 +1381,13 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
     if (k.blk2d)
       hipLaunchKernelGGL((cast_edge_kernel<T, ROWW, COLW, true>), dim3((unsigned)(segs * nstrips)),
                          block, 0, s, k);
-    else
+    else if (k.four_six) {
+      // one direction per launch (both directions' candidates in one kernel
+      // exceed the register file)
+      if constexpr (!(ROWW && COLW))
+        hipLaunchKernelGGL((cast_edge_kernel<T, ROWW, COLW, false, true>),
+                           dim3((unsigned)(segs * nstrips)), block, 0, s, k);
+    } else
       hipLaunchKernelGGL((cast_edge_kernel<T, ROWW, COLW, false>), dim3((unsigned)(segs * nstrips)),
                          block, 0, s, k);
   };
@@ -1267,6 +1420,7 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
   k.grp_align = a.grp_align;
   k.grp_T = a.grp_T;
   k.blk2d = a.blk2d;
+  k.four_six = a.four_six;
   constexpr int V = 16 / sizeof(T);
   k.vec_load = ((a.K % V) == 0) && ((reinterpret_cast<uintptr_t>(a.x) & 15) == 0);
   k.row_store4 = (a.K % 8 == 0) && ((reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0);
@@ -1284,7 +1438,8 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
   // masked row's offset, 2^31 + 15 rows, then stays within 32 bits).
   const bool grp_ok = a.grp_G == 0 || (a.grp_G <= IT_COLS && a.row_mode == 1 && a.col_mode == 2 &&
                                        a.grp_T < lim && a.M < lim);
-  const bool fast = grp_ok && k.vec_load && (a.K % IT_COLS == 0) && (a.M % 64 == 0) &&
+  // Four-over-six blocks run on the checked kernel over the whole matrix.
+  const bool fast = !a.four_six && grp_ok && k.vec_load && (a.K % IT_COLS == 0) && (a.M % 64 == 0) &&
                     (!a.q_row || (reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0) &&
                     (!a.s_row || (reinterpret_cast<uintptr_t>(a.s_row) & 15) == 0) &&
                     (!a.q_col || (reinterpret_cast<uintptr_t>(a.q_col) & 15) == 0) &&
@@ -1307,7 +1462,10 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
     k.n_istrips = k.n_isteps = 0;
   if (k.n_istrips == 0 || k.n_isteps == 0) k.n_istrips = k.n_isteps = k.half_last = 0;
   const bool rw = a.q_row != nullptr, cw = a.q_col != nullptr;
-  if (rw && cw) launch_cast_kernels<T, true, true>(k, a, s);
+  if (rw && cw && a.four_six) {
+    launch_cast_kernels<T, true, false>(k, a, s);
+    launch_cast_kernels<T, false, true>(k, a, s);
+  } else if (rw && cw) launch_cast_kernels<T, true, true>(k, a, s);
   else if (rw) launch_cast_kernels<T, true, false>(k, a, s);
   else launch_cast_kernels<T, false, true>(k, a, s);
   return hipGetLastError() == hipSuccess ? 0 : -3;

@@ -93,10 +93,10 @@ int nvfp4_group_amax_expand(float* row_amax, int64_t M, const int64_t* group_end
              : NVFP4_OK;
 }
 
-int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
-                             const float* row_amax, int col_mode, const float* col_amax,
-                             float bound, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
-                             uint8_t* s_col, const float* noop, void* stream) {
+static int quantize_impl(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
+                         const float* row_amax, int col_mode, const float* col_amax, float bound,
+                         uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                         const float* noop, void* stream, int four_six) {
   if (x == nullptr || M < 1 || K < 1) return NVFP4_ERR_ARG;
   if (M > (int64_t)1 << 40 || K > (int64_t)1 << 40) return NVFP4_ERR_ARG;
   if (in_dtype != NVFP4_BF16 && in_dtype != NVFP4_FP32) return NVFP4_ERR_ARG;
@@ -130,7 +130,24 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
   a.q_col = cw ? q_col : nullptr;
   a.s_col = cw ? s_col : nullptr;
   a.noop = noop;
+  a.four_six = four_six;
   return launch_cast(a, static_cast<hipStream_t>(stream)) ? NVFP4_ERR_HIP : NVFP4_OK;
+}
+
+int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
+                             const float* row_amax, int col_mode, const float* col_amax,
+                             float bound, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
+                             uint8_t* s_col, const float* noop, void* stream) {
+  return quantize_impl(x, in_dtype, M, K, row_mode, row_amax, col_mode, col_amax, bound, q_row,
+                       s_row, q_col, s_col, noop, stream, 0);
+}
+
+int nvfp4_quantize_4over6(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
+                          const float* row_amax, int col_mode, const float* col_amax, float bound,
+                          uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
+                          const float* noop, void* stream) {
+  return quantize_impl(x, in_dtype, M, K, row_mode, row_amax, col_mode, col_amax, bound, q_row,
+                       s_row, q_col, s_col, noop, stream, 1);
 }
 
 int nvfp4_quantize_2d(const void* x, int in_dtype, int64_t M, int64_t K, const float* tensor_amax,

@@ -44,6 +44,8 @@ struct CastArgs {
   int64_t grp_G = 0, grp_align = 16, grp_T = 0;
   // 2-D 16 x 16 blocks (row and column mode TENSOR, one amax)
   int blk2d = 0;
+  // four-over-six block scales (1x16 blocks)
+  int four_six = 0;
 };
 int launch_cast(const CastArgs& a, hipStream_t s);
 
