@@ -100,6 +100,18 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
     res["quantize_2d_bf16_8192x28672"] = _row(timed(f2d, n) * 1e3, cb2,
                                               "X read once, both copies written")
     del out
+    # four-over-six block scales, both copies (row and column amax given;
+    # one launch per direction, so X is read twice)
+    p.nvfp4_amax_rowcol(xs[0], ra, ca)
+    out = p.empty_outputs(M, K, dev)
+    f46 = lambda i: p.nvfp4_quantize_4over6(xs[i & 1], p.NVFP4_AMAX_LINE, ra, p.NVFP4_AMAX_LINE, ca,
+                                            256.0, out["q_row"], out["s_row"], out["q_col"],
+                                            out["s_col"])
+    f46(0)
+    res["quantize_4over6_bf16_8192x28672"] = _row(
+        timed(f46, 5) * 1e3, 2 * xb + 4 * (M + K) + 2 * (M * (K // 2) + M * (K // 16)),
+        "X read once per direction, both copies written")
+    del out
     # rowwise codes and their BF16 dequantization in one pass (row amax given)
     p.nvfp4_amax_rowcol(xs[0], ra)
     qr = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
