@@ -26,6 +26,7 @@
 #include "nvfp4_launch.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace nvfp4 {
 
@@ -967,7 +968,8 @@ __device__ __forceinline__ WaveRows grouped_wave_rows(const ITSmem& sm, int G, u
   return w;
 }
 
-// VAR: 0 = 1x16 blocks, 1 = grouped tokens (1x16), 2 = 2-D 16 x 16 blocks
+// VAR: 0 = 1x16 blocks, 1 = grouped tokens (1x16), 2 = 2-D 16 x 16 blocks,
+// 3 = four-over-six 1x16 blocks (one direction per launch)
 template <typename T, bool ROWW, bool COLW, int VAR>
 __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_kernel(const CastK p) {
   if (p.noop != nullptr && *p.noop == 1.0f) return;
@@ -1158,11 +1160,16 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
         if (vn < n_v) prefetch(m0n + (vn & 1) * IT_SUB, c0n, WaveRows{0, 0u, 0u, 0u, 0u});
       }
     };
-    if constexpr (B2D)
+    if constexpr (B2D) {
       process_block_2d<T, ROWW, COLW>(w, st, a2d, s2d, p.F_inv, mid);
-    else
+    } else if constexpr (VAR == 3) {
+      mid();
+      process_block_46<T, ROWW, COLW>(w, st, h, par, LdsTab{sm.ra[wv], sm.rs[wv], 0}, ctab,
+                                      p.F_inv);
+    } else {
       process_block_batched<T, ROWW, COLW>(w, st, h, par, LdsTab{sm.ra[wv], sm.rs[wv], 0}, ctab,
                                            p.F_inv, mid);
+    }
     __syncthreads();  // the sub-step's staged outputs are complete
 
     if constexpr (ROWW) {  // 128 rows x 16 B
@@ -1324,19 +1331,22 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
 template <typename T, bool ROWW, bool COLW, int VAR>
 static int interior_grid() {
   // resident interior workgroups on the device (a multiple of 8), per device
-  static int cache[64] = {0};
+  // (host threads may fill an entry concurrently, with the same value)
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] == 0) {
+  int g = cache[dev].load(std::memory_order_relaxed);
+  if (g == 0) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW, VAR>), 256, 0) !=
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
-    cache[dev] = std::max(IT_XCDS, (num_cus() * per_cu) / IT_XCDS * IT_XCDS);
+    g = std::max(IT_XCDS, (num_cus() * per_cu) / IT_XCDS * IT_XCDS);
+    cache[dev].store(g, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return g;
 }
 
 template <typename T, bool ROWW, bool COLW>
@@ -1354,6 +1364,12 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
       const int64_t G = interior_grid<T, ROWW, COLW, 2>();
       hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 2>), dim3((unsigned)G), dim3(256), 0,
                          s, k);
+    } else if (k.four_six) {
+      if constexpr (!(ROWW && COLW)) {
+        const int64_t G = interior_grid<T, ROWW, COLW, 3>();
+        hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 3>), dim3((unsigned)G), dim3(256),
+                           0, s, k);
+      }
     } else {
       const int64_t G = interior_grid<T, ROWW, COLW, 0>();
       hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 0>), dim3((unsigned)G), dim3(256), 0,
@@ -1438,8 +1454,7 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
   // masked row's offset, 2^31 + 15 rows, then stays within 32 bits).
   const bool grp_ok = a.grp_G == 0 || (a.grp_G <= IT_COLS && a.row_mode == 1 && a.col_mode == 2 &&
                                        a.grp_T < lim && a.M < lim);
-  // Four-over-six blocks run on the checked kernel over the whole matrix.
-  const bool fast = !a.four_six && grp_ok && k.vec_load && (a.K % IT_COLS == 0) && (a.M % 64 == 0) &&
+  const bool fast = grp_ok && k.vec_load && (a.K % IT_COLS == 0) && (a.M % 64 == 0) &&
                     (!a.q_row || (reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0) &&
                     (!a.s_row || (reinterpret_cast<uintptr_t>(a.s_row) & 15) == 0) &&
                     (!a.q_col || (reinterpret_cast<uintptr_t>(a.q_col) & 15) == 0) &&
