@@ -16,9 +16,14 @@ amax pass), and the pairs' average gives the roofline fraction (algorithmic
 bytes of one cast launch / that duration, against 8 TB/s). Two more regions of
 K back-to-back launches of one kernel each (amax pass, cast pass) are reported
 beside it; a cast right after another cast also pays for the previous cast's
-write-back, so that figure runs higher and varies more from GPU to GPU. Also
-reported: the dequantize kernel's bandwidth and the CPU oracle timed on a
-bounded sample of the same workload on the host cores.
+write-back, so that figure runs higher and varies more from GPU to GPU. A
+bounded spin kernel queued ahead of each timed region lets the host enqueue
+the whole region before the GPU reaches it. Also reported: the dequantize
+kernel's bandwidth, the other kernels of the path on the workloads they serve
+(two-kernel and per-tensor amax, 2-D tiles, four-over-six, quantize +
+dequantize, the FP32 edge matrix, grouped tokens, and the two small matrices
+cold), and the CPU oracle timed on a bounded sample of the same workload on
+the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration   (plain torch copy, for counter scaling)
