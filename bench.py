@@ -162,7 +162,7 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
     moe(0)
     mb = 2 * M * K * 2 + 4 * 4 * M + 8 * ge.numel() + M * ((K + 1) // 2) + M * ((K + 15) // 16) \
         + K * ((M + 1) // 2) + K * ((M + 15) // 16)
-    res["moe_%dx%d_amax_expand_cast" % (M, K)] = _row(timed(moe, n) * 1e3, mb,
+    res["moe_%dx%d_amax_expand_cast" % (M, K)] = _row(timed(moe, n, 3) * 1e3, mb,
                                                        "X read by the amax and the cast passes")
     del x
 
@@ -248,8 +248,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time the CPU oracle is run for (whole passes)")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--hold-ms", type=float, default=100.0,
-                    help="length of the spin kernel queued ahead of each timed region")
+    ap.add_argument("--hold-ms", type=float, default=None,
+                    help="length of the spin kernel queued ahead of each timed region "
+                         "(default: 1 ms + 1.5 x the host's measured time to enqueue it)")
     return ap.parse_args()
 
 
@@ -307,7 +308,9 @@ def main():
     # A bounded spin kernel at the head of the stream keeps the GPU busy
     # while the host enqueues a whole timed region, so the region's kernels
     # run back to back from the queue with no launch gaps, also when a
-    # profiler slows every host-side launch. Its length is calibrated once.
+    # profiler slows every host-side launch. Its length follows the host's
+    # measured cost per launch (a longer wait than needed idles the GPU, which
+    # then starts the region at a lower clock).
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda._sleep(1000)
@@ -318,17 +321,20 @@ def main():
     torch.cuda.synchronize()
     sleep_cycles_per_ms = (1 << 20) / max(e0.elapsed_time(e1), 1e-3)
 
-    def hold_queue(ms):
+    host_ms_per_call = [0.05]  # refined by the warm-up below
+
+    def hold_queue(n_calls):
+        ms = args.hold_ms if args.hold_ms is not None else 1.0 + 1.5 * n_calls * host_ms_per_call[0]
         torch.cuda._sleep(int(ms * sleep_cycles_per_ms))
 
-    def timed(fn, n):
+    def timed(fn, n, calls_per_fn=1):
         """Average time of fn(0..n-1) launched back to back, HIP events on the
         launch stream at the two ends of the region only (an event between two
         kernels would add a gap of its own)."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        hold_queue(args.hold_ms)
+        hold_queue(n * calls_per_fn)
         e0.record()
         for i in range(n):
             fn(i)
@@ -340,16 +346,24 @@ def main():
         amax(i)
         cast(i)
     torch.cuda.synchronize()
+    # the host's cost per launch, from a few more (untimed) steps enqueued
+    # after the warm-up
+    t_host = time.perf_counter()
+    for i in range(4):
+        amax(i)
+        cast(i)
+    host_ms_per_call[0] = (time.perf_counter() - t_host) * 1e3 / 8
+    torch.cuda.synchronize()
 
     K_steps = args.steps
     # headline: K whole steps
-    ms_per_step = timed(lambda i: (amax(i), cast(i)), K_steps)
+    ms_per_step = timed(lambda i: (amax(i), cast(i)), K_steps, 2)
     # per-kernel regions: the same launches, one kind at a time
     # the cast inside the step: an event pair around each cast, after its amax
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K_steps)]
     torch.cuda.synchronize()
-    hold_queue(args.hold_ms)
+    hold_queue(4 * K_steps)
     for i in range(K_steps):
         amax(i)
         ev[i][0].record()

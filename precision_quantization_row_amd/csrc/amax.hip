@@ -85,14 +85,13 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
   // (rows past rend are skipped; with M % 128 == 0 and tr a multiple of 32
   // that only happens for RU = 4 and 32-row tiles)
   //
-  // The first three quarters of the tile's rows are read with non-temporal
-  // loads, the last quarter with ordinary ones: X is read again by the cast
-  // right after this pass, and what this pass reads last is what the caches
-  // still hold then. Measured on 8192 x 28672 (same GPU, step = this pass +
-  // the cast): all ordinary 226-228 us, 1/2 streamed 218-223, 3/4 streamed
-  // 217-221, 7/8 225, all streamed 227 (this pass alone 85 -> 78 us, but the
-  // cast loses the cached rows).
-  const int64_t r_stream = r0 + (3 * tr) / 4;
+  // The first half of the tile's rows is read with non-temporal loads, the
+  // second half with ordinary ones: X is read again by the cast right after
+  // this pass, and what this pass reads last is what the caches still hold
+  // then. Measured on 8192 x 28672 (same GPU, step = this pass + the cast):
+  // streamed fraction 0: 217 us, 1/4: 209, 3/8: 207, 1/2: 205-207, 5/8: 207,
+  // 3/4: 208-209 (this pass alone: 87 us with none streamed, 79.6 with half).
+  const int64_t r_stream = r0 + tr / 2;
   for (int64_t rb = r0 + slot; rb < rend; rb += 16 * FUSED_RU) {
     uint4 v[FUSED_RU][FUSED_NC];
     const bool stream = rb < r_stream;
