@@ -407,11 +407,25 @@ def main():
             oracle.quantize_colwise(x_host, oracle.MODE_LINE, ca_o, bound)
             reps += 1
         dt = time.perf_counter() - t0
+        threads = oracle.max_threads()
+        # the same pass on one thread, over a sixteenth of the rows
+        rows1 = max(16, rows // 16)
+        x1 = np.ascontiguousarray(x_host[:rows1])
+        oracle.set_threads(1)
+        t1 = time.perf_counter()
+        ra_o, ca_o = oracle.amax_rows(x1), oracle.amax_cols(x1)
+        oracle.quantize_rowwise(x1, oracle.MODE_LINE, ra_o, bound)
+        oracle.quantize_colwise(x1, oracle.MODE_LINE, ca_o, bound)
+        dt1 = time.perf_counter() - t1
+        oracle.set_threads(threads)
         cpu = {"value": round(reps * workloads.algorithmic_bytes(rows, K, 2) / dt / 1e9, 4),
-               "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+               "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"{reps} pass(es) over the first {rows} rows x {K} columns of the same "
                          f"matrix (as its own {rows}x{K} input): amax rows+cols, then both "
-                         f"quantize directions; {dt:.1f} s wall"}
+                         f"quantize directions; {dt:.1f} s wall",
+               "value_1_thread": round(workloads.algorithmic_bytes(rows1, K, 2) / dt1 / 1e9, 4),
+               "sample_1_thread": f"one pass over the first {rows1} rows x {K} columns on 1 "
+                                  f"thread; {dt1:.1f} s wall"}
 
     rec = {
         "metric": METRIC,

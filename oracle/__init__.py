@@ -67,6 +67,7 @@ def _load():
         "orc_e2m1_encode_array": (None, [f32p, i64, u8p]),
         "orc_e4m3_encode_array": (None, [f32p, i64, u8p]),
         "orc_max_threads": (c_int, []),
+        "orc_set_threads": (None, [c_int]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -85,6 +86,12 @@ def _f32(a) -> np.ndarray:
 
 def _p(a: np.ndarray, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def set_threads(n: int) -> None:
+    """Threads the OpenMP loops over lines use from now on (the bits do not
+    depend on it)."""
+    _load().orc_set_threads(int(n))
 
 
 def max_threads() -> int:

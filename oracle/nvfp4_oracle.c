@@ -480,6 +480,8 @@ void orc_e4m3_encode_array(const float *v, int64_t n, uint8_t *out) {
 #ifdef _OPENMP
 #include <omp.h>
 int orc_max_threads(void) { return omp_get_max_threads(); }
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int orc_max_threads(void) { return 1; }
+void orc_set_threads(int n) { (void)n; }
 #endif
