@@ -89,6 +89,15 @@ def test_validation_rejects_before_launch():
     for M, K in ((0, 32), (32, 0), (-1, 32)):
         assert lib.nvfp4_quantize_transpose(_fake(), 0, M, K, 1, _fake(), 1, _fake(), f(448.0),
                                             _fake(), _fake(), _fake(), _fake(), None, None) == E
+    # four-over-six: the same validation as the plain quantize
+    q46 = lambda bound, M=32, rm=1, cm=1, qr=_fake(), sr=_fake(), qc=_fake(), sc=_fake(), \
+        ra=_fake(), ca=_fake(), x=_fake(), dt=0: lib.nvfp4_quantize_4over6(
+            x, dt, M, 32, rm, ra, cm, ca, f(bound), qr, sr, qc, sc, None, None)
+    for bad in (0.0, -1.0, 449.0, float("nan")):
+        assert q46(bad) == E
+    for kw in (dict(M=0), dict(x=None), dict(dt=4), dict(qr=None, sr=None, qc=None, sc=None),
+               dict(sr=None), dict(ca=None), dict(rm=2), dict(cm=3)):
+        assert q46(256.0, **kw) == E, kw
     # dequantize
     d = lambda mode=1, out=0, bound=448.0, R=4, C=16: lib.nvfp4_dequantize(
         _fake(), _fake(), R, C, mode, _fake(), f(bound), _fake(), out, None, None)
