@@ -970,7 +970,7 @@ __device__ __forceinline__ WaveRows grouped_wave_rows(const ITSmem& sm, int G, u
 
 // VAR: 0 = 1x16 blocks, 1 = grouped tokens (1x16), 2 = 2-D 16 x 16 blocks,
 // 3 = four-over-six 1x16 blocks (one direction per launch)
-template <typename T, bool ROWW, bool COLW, int VAR>
+template <typename T, bool ROWW, bool COLW, int VAR, bool SPLIT = false>
 __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_kernel(const CastK p) {
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   constexpr bool GRP = VAR == 1, B2D = VAR == 2;
@@ -1003,11 +1003,34 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     s2d = global_encode_scale(a2d, p.F);
   }
 
-  // sub-step v: macro tile origin (m0, c0); false when outside the interior
-  // (uniform per workgroup, the same for both sub-steps of a tile)
+  // The last round of macro tiles: when it holds at most half as many tiles
+  // as the XCD has workgroups, its tiles are split into their two 128-row
+  // halves, one per workgroup, each flushed on its own (64 B of transposed
+  // codes and 8 scale bytes per column), so that twice as many workgroups
+  // share the round.
+  const int64_t rounds = (ntiles_x + per - 1) / per;
+  const int64_t last_n = ntiles_x - (rounds - 1) * per;  // tiles in the last round
+  // (compiled in only where the host expects it: the extra schedule logic
+  // costs the plain variant registers)
+  const bool split_last = SPLIT && rounds > 0 && 2 * last_n <= per;
+
+  // sub-step v: macro tile origin (m0, c0), which 128-row half of it (sub)
+  // and whether that half is flushed on its own (solo: a split half, or the
+  // 128-row last macro row); false when outside the interior (uniform per
+  // workgroup)
   // (32-bit index arithmetic: the host sends only grids whose tile counts fit)
-  auto tile_of = [&](int64_t v, int64_t& m0, int64_t& c0) -> bool {
-    const uint32_t t = (uint32_t)(v >> 1) * (uint32_t)per + (uint32_t)jw;
+  auto tile_of = [&](int64_t v, int64_t& m0, int64_t& c0, int& sub, bool& solo) -> bool {
+    uint32_t t;
+    if (split_last && (v >> 1) == rounds - 1) {
+      if ((v & 1) || jw >= 2 * last_n) return false;
+      t = (uint32_t)(rounds - 1) * (uint32_t)per + (uint32_t)(jw >> 1);
+      sub = (int)(jw & 1);
+      solo = true;
+    } else {
+      t = (uint32_t)(v >> 1) * (uint32_t)per + (uint32_t)jw;
+      sub = (int)(v & 1);
+      solo = false;
+    }
     // strip groups of sg strips (the XCD's last group may hold fewer), each
     // walked macro row by macro row with its strips side by side
     const uint32_t sg = (uint32_t)p.sgroup, gsz = sg * (uint32_t)nmr;
@@ -1017,11 +1040,12 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     const int64_t strip = xcd * spx + g * sg + qs;
     m0 = (int64_t)r * IT_MACRO;
     c0 = strip * IT_COLS;
-    const bool cut = p.half_last && r == (uint32_t)nmr - 1 && (v & 1);  // half macro tile
-    return t < (uint64_t)ntiles_x && strip < nstrips && !cut;
+    const bool last_half = p.half_last && r == (uint32_t)nmr - 1;  // a 128-row macro row
+    solo = solo || last_half;
+    return t < (uint64_t)ntiles_x && strip < nstrips && !(last_half && sub == 1);
   };
-  auto next_sub = [&](int64_t v, int64_t& m0, int64_t& c0) -> int64_t {
-    while (v < n_v && !tile_of(v, m0, c0)) ++v;
+  auto next_sub = [&](int64_t v, int64_t& m0, int64_t& c0, int& sub, bool& solo) -> int64_t {
+    while (v < n_v && !tile_of(v, m0, c0, sub, solo)) ++v;
     return v;
   };
   const uint32_t vo = (uint32_t)h * 16u * rowbytes + (uint32_t)(8 * L * sizeof(T));
@@ -1067,14 +1091,16 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
 
   int sbuf = 0, mbuf = 0;
   int64_t m0 = 0, c0 = 0, c0_tab = -1;
-  int64_t v = next_sub(0, m0, c0);
+  int cur_sub = 0;
+  bool cur_solo = false;
+  int64_t v = next_sub(0, m0, c0, cur_sub, cur_solo);
   WaveRows gm{0, 0u, 0u, 0u, 0u};  // grouped: the current sub-step's rows
   if constexpr (GRP) {
-    if (v < n_v) gm = grp_map(m0 + (v & 1) * IT_SUB);
+    if (v < n_v) gm = grp_map(m0 + cur_sub * IT_SUB);
   }
-  if (v < n_v) prefetch(m0 + (v & 1) * IT_SUB, c0, gm);
+  if (v < n_v) prefetch(m0 + cur_sub * IT_SUB, c0, gm);
   while (v < n_v) {
-    const int sub = (int)(v & 1);
+    const int sub = cur_sub;
     const int64_t rs = m0 + sub * IT_SUB;
     // column amax / S_enc: the strip's table in LDS (modes 0 and 1, filled
     // when the strip changes), or the group amax of the lane's 16-row block
@@ -1133,10 +1159,12 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
       }
     }
     int64_t m0n = 0, c0n = 0;
-    const int64_t vn = next_sub(v + 1, m0n, c0n);
+    int subn = 0;
+    bool solon = false;
+    const int64_t vn = next_sub(v + 1, m0n, c0n, subn, solon);
     WaveRows gmn{0, 0u, 0u, 0u, 0u};
     if constexpr (GRP) {
-      if (vn < n_v) gmn = grp_map(m0n + (vn & 1) * IT_SUB);
+      if (vn < n_v) gmn = grp_map(m0n + subn * IT_SUB);
     }
 
     StoreIT st;
@@ -1155,9 +1183,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     }
     auto mid = [&]() {
       if constexpr (GRP) {
-        if (vn < n_v) prefetch(m0n + (vn & 1) * IT_SUB, c0n, gmn);
+        if (vn < n_v) prefetch(m0n + subn * IT_SUB, c0n, gmn);
       } else {
-        if (vn < n_v) prefetch(m0n + (vn & 1) * IT_SUB, c0n, WaveRows{0, 0u, 0u, 0u, 0u});
+        if (vn < n_v) prefetch(m0n + subn * IT_SUB, c0n, WaveRows{0, 0u, 0u, 0u, 0u});
       }
     };
     if constexpr (B2D) {
@@ -1178,10 +1206,10 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
             *reinterpret_cast<const uint4*>(&sm.sr[sbuf][tid][0]);
     }
     sbuf ^= 1;
-    // a half macro tile (the last macro row of a matrix with M % 256 = 128)
-    // is flushed after its only sub-step: 64 B of codes and 8 scale bytes per
-    // column
-    const bool half = p.half_last && m0 == (nmr - 1) * IT_MACRO;
+    // a half flushed on its own (the last macro row of a matrix with
+    // M % 256 = 128, or a split tile of the last round) writes 64 B of codes
+    // and 8 scale bytes per column, those of its own 128 rows
+    const bool half = cur_solo;
     if (COLW && (sub == 1 || half)) {
       // 256 columns x 128 B of transposed codes: 8 lanes per column, whole
       // lines, slots restored to row order
@@ -1189,7 +1217,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
       for (int it = 0; it < IT_COLS * 8 / 256; ++it) {
         const int pidx = tid + 256 * it;
         const int c = pidx >> 3, t = pidx & 7;
-        if (half && t >= 4) continue;
+        if (half && (t >> 2) != sub) continue;
         const int f = (c >> 3) & 15;
         u32x4 q = *reinterpret_cast<const u32x4*>(&sm.qc[mbuf][c ^ (f & 1)][16 * (t ^ (f >> 1))]);
         if (f & 1) q = (u32x4){q.z, q.w, q.x, q.y};
@@ -1205,8 +1233,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
           *reinterpret_cast<u32x4*>(dst) = q;
         } else {
           uint32_t* d4 = reinterpret_cast<uint32_t*>(dst);
-          d4[0] = q.x; d4[1] = q.y;
-          if (!half) { d4[2] = q.z; d4[3] = q.w; }
+          if (!half || sub == 0) { d4[0] = q.x; d4[1] = q.y; }
+          if (!half || sub == 1) { d4[2] = q.z; d4[3] = q.w; }
         }
       }
       mbuf ^= 1;
@@ -1214,6 +1242,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     v = vn;
     m0 = m0n;
     c0 = c0n;
+    cur_sub = subn;
+    cur_solo = solon;
     if constexpr (GRP) gm = gmn;
   }
 }
@@ -1328,7 +1358,7 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
   }
 }
 
-template <typename T, bool ROWW, bool COLW, int VAR>
+template <typename T, bool ROWW, bool COLW, int VAR, bool SPLIT = false>
 static int interior_grid() {
   // resident interior workgroups on the device (a multiple of 8), per device
   // (host threads may fill an entry concurrently, with the same value)
@@ -1339,7 +1369,7 @@ static int interior_grid() {
   if (g == 0) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW, VAR>), 256, 0) !=
+            &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW, VAR, SPLIT>), 256, 0) !=
             hipSuccess ||
         per_cu < 1)
       per_cu = 1;
@@ -1355,11 +1385,25 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
   const int64_t ntiles = k.n_istrips * k.n_isteps;
   if (ntiles > 0) {
     // all resident workgroups: a partly idle last round costs less than
-    // fewer waves per CU
+    // fewer waves per CU. Whether the last round splits its tiles into halves
+    // (at most half as many tiles as an XCD has workgroups) picks the
+    // kernel variant that carries that schedule.
+    auto split = [&](int64_t G) {
+      const int64_t per = G / IT_XCDS;
+      const int64_t ntx = k.n_isteps * ((k.n_istrips + IT_XCDS - 1) / IT_XCDS);
+      const int64_t rounds = (ntx + per - 1) / per;
+      return per > 0 && rounds > 0 && 2 * (ntx - (rounds - 1) * per) <= per;
+    };
     if (k.grp_G > 0) {
-      const int64_t G = interior_grid<T, ROWW, COLW, 1>();
-      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 1>), dim3((unsigned)G), dim3(256), 0,
-                         s, k);
+      if (split(interior_grid<T, ROWW, COLW, 1>())) {
+        const int64_t G = interior_grid<T, ROWW, COLW, 1, true>();
+        hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 1, true>), dim3((unsigned)G),
+                           dim3(256), 0, s, k);
+      } else {
+        const int64_t G = interior_grid<T, ROWW, COLW, 1>();
+        hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 1>), dim3((unsigned)G), dim3(256),
+                           0, s, k);
+      }
     } else if (k.blk2d) {
       const int64_t G = interior_grid<T, ROWW, COLW, 2>();
       hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 2>), dim3((unsigned)G), dim3(256), 0,
@@ -1370,6 +1414,10 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 3>), dim3((unsigned)G), dim3(256),
                            0, s, k);
       }
+    } else if (split(interior_grid<T, ROWW, COLW, 0>())) {
+      const int64_t G = interior_grid<T, ROWW, COLW, 0, true>();
+      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 0, true>), dim3((unsigned)G),
+                         dim3(256), 0, s, k);
     } else {
       const int64_t G = interior_grid<T, ROWW, COLW, 0>();
       hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 0>), dim3((unsigned)G), dim3(256), 0,
