@@ -1405,14 +1405,26 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
                            0, s, k);
       }
     } else if (k.blk2d) {
-      const int64_t G = interior_grid<T, ROWW, COLW, 2>();
-      hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 2>), dim3((unsigned)G), dim3(256), 0,
-                         s, k);
+      if (split(interior_grid<T, ROWW, COLW, 2>())) {
+        const int64_t G = interior_grid<T, ROWW, COLW, 2, true>();
+        hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 2, true>), dim3((unsigned)G),
+                           dim3(256), 0, s, k);
+      } else {
+        const int64_t G = interior_grid<T, ROWW, COLW, 2>();
+        hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 2>), dim3((unsigned)G), dim3(256),
+                           0, s, k);
+      }
     } else if (k.four_six) {
       if constexpr (!(ROWW && COLW)) {
-        const int64_t G = interior_grid<T, ROWW, COLW, 3>();
-        hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 3>), dim3((unsigned)G), dim3(256),
-                           0, s, k);
+        if (split(interior_grid<T, ROWW, COLW, 3>())) {
+          const int64_t G = interior_grid<T, ROWW, COLW, 3, true>();
+          hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 3, true>), dim3((unsigned)G),
+                             dim3(256), 0, s, k);
+        } else {
+          const int64_t G = interior_grid<T, ROWW, COLW, 3>();
+          hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 3>), dim3((unsigned)G),
+                             dim3(256), 0, s, k);
+        }
       }
     } else if (split(interior_grid<T, ROWW, COLW, 0>())) {
       const int64_t G = interior_grid<T, ROWW, COLW, 0, true>();
