@@ -393,12 +393,8 @@ __global__ void __launch_bounds__(256) grouped_row_amax_kernel(const T* __restri
   const int64_t nwaves = ((int64_t)gridDim.x * blockDim.x) >> 6;
   constexpr int V = 16 / sizeof(T);
   for (int64_t r = wave; r < T_rows; r += nwaves) {
-    const uint32_t g = groups_ending_by(e.tok, (uint32_t)r);
-    if (g >= (uint32_t)G) break;  // this and every later row lie past the groups
-    const uint32_t t0 = g ? group_end_at(e.tok, g - 1) : 0u;
-    const uint32_t p0 = g ? group_end_at(e.pad, g - 1) : 0u;
-    const int64_t pr = (int64_t)p0 + (r - (int64_t)t0);
-    if (pr >= M_out) continue;
+    // the row's loads go out first; its place in the padded layout is looked
+    // up while they are in flight (a row past the groups is read and dropped)
     const T* row = x + r * K;
     uint32_t m = 0u;
     if (VEC) {
@@ -412,7 +408,12 @@ __global__ void __launch_bounds__(256) grouped_row_amax_kernel(const T* __restri
       }
     }
     for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-    if (lane == 0) ra[pr] = __uint_as_float(m);
+    const uint32_t g = groups_ending_by(e.tok, (uint32_t)r);
+    if (g >= (uint32_t)G) break;  // this and every later row lie past the groups
+    const uint32_t t0 = g ? group_end_at(e.tok, g - 1) : 0u;
+    const uint32_t p0 = g ? group_end_at(e.pad, g - 1) : 0u;
+    const int64_t pr = (int64_t)p0 + (r - (int64_t)t0);
+    if (lane == 0 && pr < M_out) ra[pr] = __uint_as_float(m);
   }
 }
 
@@ -550,7 +551,8 @@ namespace nvfp4 {
 int launch_grouped_amax(const void* x, int in_dtype, int64_t T, int64_t K, const int64_t* grows,
                         int64_t G, int64_t align, int64_t M_out, float* ra, const float* noop,
                         hipStream_t s) {
-  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((T + 3) / 4, (int64_t)num_cus() * 16));
+  // a few rows per wave, so that its group-table setup is shared
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((T + 3) / 4, (int64_t)num_cus() * 4));
   const bool vec16 = ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
   const int g = (int)G;
   if (in_dtype == 0) {
