@@ -141,8 +141,8 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
  * in order, then the two sums; the max-6 scale on a tie). The chosen byte is
  * an ordinary E4M3 block scale, so nvfp4_dequantize decodes the result
  * unchanged. Bound 256 keeps the max-4 scale of a block that holds the line
- * amax below 448 (6/4 * 256 = 384). Runs on the checked kernel over the
- * whole matrix (it computes both candidates per block). */
+ * amax below 448 (6/4 * 256 = 384). Both copies requested: one launch per
+ * copy (X is read once for each); it computes both candidates per block. */
 int nvfp4_quantize_4over6(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
                           const float* row_amax, int col_mode, const float* col_amax, float bound,
                           uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
