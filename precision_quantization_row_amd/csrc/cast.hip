@@ -837,14 +837,19 @@ constexpr int IT_SUB = 128;                  // rows per sub-step
 constexpr int IT_MACRO = 2 * IT_SUB;         // rows per macro tile
 constexpr int IT_XCDS = 8;
 
+// Without the columnwise copy the transposed staging shrinks to a stub (the
+// code that touches it is never reached), so rowwise-only launches fit more
+// workgroups per CU.
+template <bool COLW>
 struct ITSmem {
+  static constexpr int QCOLS = COLW ? IT_COLS : 1;
   // transposed codes of the macro tile, [buf][storage column][16 slots x 8 B].
   // Slot s holds rows 16s .. +16 of the column. Column c is stored at
   // c ^ ((c >> 3) & 1) and slot s at position s ^ ((c >> 3) & 15), so the 64
   // lanes of one store instruction spread over all 64 banks.
-  uint8_t qc[2][IT_COLS][128];
+  uint8_t qc[2][QCOLS][128];
   // transposed scales, [buf][entry][16 blocks]; column 8L + k at entry 32k + L
-  uint8_t sc[2][IT_COLS][16];
+  uint8_t sc[2][QCOLS][16];
   // rowwise scales of a sub-step, [buf][row][16 blocks]
   uint8_t sr[2][IT_SUB][16];
   // per-wave row amax / S_enc of the wave's 32 rows
@@ -894,7 +899,8 @@ struct StoreIT {
 // saturating at 2^31 - 1 (the host sends only T, M < 2^31 here, so a
 // saturated end lies past every row the kernel touches); entries from G on
 // hold 0xFFFFFFFF in gpad. All 256 threads.
-__device__ __forceinline__ void build_group_table32(ITSmem& sm, const int64_t* rows, int G,
+template <class SM>
+__device__ __forceinline__ void build_group_table32(SM& sm, const int64_t* rows, int G,
                                                     int64_t align) {
   constexpr uint32_t CL = 0x7FFFFFFFu;
   const int t = threadIdx.x;
@@ -932,7 +938,8 @@ struct WaveRows {
   uint32_t lim, d1, n0, n1;
 };
 
-__device__ __forceinline__ WaveRows grouped_wave_rows(const ITSmem& sm, int G, uint32_t T,
+template <class SM>
+__device__ __forceinline__ WaveRows grouped_wave_rows(const SM& sm, int G, uint32_t T,
                                                       int lane, uint32_t pr0) {
   // group of a padded row = the number of groups that end at or before it
   const u32x4 e = *reinterpret_cast<const u32x4*>(&sm.gpad[4 * lane]);
@@ -975,7 +982,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   constexpr bool GRP = VAR == 1, B2D = VAR == 2;
   constexpr int NW = Blk<T>::NW;
-  __shared__ __attribute__((aligned(16))) ITSmem sm;
+  __shared__ __attribute__((aligned(16))) ITSmem<COLW> sm;
   const T* __restrict__ x = static_cast<const T*>(p.x);
   const int tid = threadIdx.x;
   // The wave index is uniform across a wave; reading it into a scalar register
