@@ -1078,8 +1078,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
   // The first PF rows of each half of the wave's next sub-step are loaded while
   // the current one's block scales and codes are computed (BF16: 32 registers;
   // FP32 has none to spare). Loading all 16 rows ahead needs 32 more registers
-  // than a wave has at 2 waves per SIMD and ends up slower.
-  constexpr int PF = sizeof(T) == 2 ? 8 : 0;
+  // than the 1x16 code has at 2 waves per SIMD and ends up slower; the 2-D
+  // code, which cannot start before all 16 rows are in, has them to spare.
+  constexpr int PF = sizeof(T) == 2 ? (B2D ? 16 : 8) : 0;
   uint32_t pf[PF > 0 ? PF : 1][NW];
   auto prefetch = [&](int64_t rs, int64_t c0, WaveRows m) {
     if constexpr (PF > 0) {
