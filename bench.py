@@ -237,8 +237,10 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 1000 steps take about 0.2 s; a region of 100 reads 1-2 % slower per
+    # step (a fixed cost of a few hundred microseconds where a region starts)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the other kernels of the path (two-kernel amax, per-tensor "

@@ -1090,9 +1090,13 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
 #pragma unroll
         for (int i = 0; i < PF; ++i) grp_load(rn, gv, gn, i, pf[i]);
       } else {
+        // the loads leave ahead of the other wave's arithmetic on the SIMD
+        // (not for four-over-six, which is bound by that arithmetic)
         const __amdgpu_buffer_rsrc_t rn = wave_rows(rs, c0);
+        if constexpr (VAR != 3) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int i = 0; i < PF; ++i) load_row_buf<T>(rn, vo, (uint32_t)i * rowbytes, pf[i]);
+        if constexpr (VAR != 3) __builtin_amdgcn_s_setprio(0);
       }
     }
   };
@@ -1156,6 +1160,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
       }
     } else {
       const __amdgpu_buffer_rsrc_t rx = wave_rows(rs, c0);
+      if constexpr (VAR != 3) __builtin_amdgcn_s_setprio(2);  // as in the prefetch
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (i < PF) {
@@ -1165,6 +1170,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
           load_row_buf<T>(rx, vo, (uint32_t)i * rowbytes, w[i]);
         }
       }
+      if constexpr (VAR != 3) __builtin_amdgcn_s_setprio(0);
     }
     int64_t m0n = 0, c0n = 0;
     int subn = 0;
