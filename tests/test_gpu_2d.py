@@ -141,6 +141,14 @@ def test_2d_full_size_sampled_bands():
         assert_same(f"s_col band {band}", to_np(out["s_col"][:, band:band + 1]), wsc)
 
 
+def test_2d_two_full_rounds_every_byte():
+    """8192 x 8192 BF16: 128 macro tiles per XCD's strips, two full rounds of
+    the resident grid on a 256-CU GPU (no split last round), so every
+    workgroup carries its next tile's rows, loaded ahead, across a tile
+    boundary. Every byte of both copies against the oracle."""
+    _check("two rounds", _matrix(8192, 8192, torch.bfloat16, seed=88))
+
+
 @pytest.mark.parametrize("M,K", [(256, 320), (512, 2880)])
 def test_2d_columns_past_the_last_strip(M, K):
     _check("partial strip", _matrix(M, K, torch.bfloat16, seed=M + K))
