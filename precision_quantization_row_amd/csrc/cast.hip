@@ -1213,6 +1213,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
                                            p.F_inv, mid);
     }
     __syncthreads();  // the sub-step's staged outputs are complete
+    // the flush's stores, too, go out ahead of the other workgroup's arithmetic
+    if constexpr (VAR != 3) __builtin_amdgcn_s_setprio(1);
 
     if constexpr (ROWW) {  // 128 rows x 16 B
       if (tid < IT_SUB)
@@ -1253,6 +1255,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
       }
       mbuf ^= 1;
     }
+    if constexpr (VAR != 3) __builtin_amdgcn_s_setprio(0);
     v = vn;
     m0 = m0n;
     c0 = c0n;
