@@ -66,6 +66,13 @@ def _load():
         "orc_group_amax_expand": (None, [f32p, i64p, i64, f32p]),
         "orc_e2m1_encode_array": (None, [f32p, i64, u8p]),
         "orc_e4m3_encode_array": (None, [f32p, i64, u8p]),
+        "orc_bf16_round": (ctypes.c_uint16, [c_f]),
+        "orc_bf16_round_array": (None, [f32p, i64, ctypes.POINTER(ctypes.c_uint16)]),
+        "orc_e2m1_encode_bits": (None, [ctypes.c_uint32, i64, u8p]),
+        "orc_e4m3_encode_bits": (None, [ctypes.c_uint32, i64, u8p]),
+        "orc_bf16_round_bits": (None, [ctypes.c_uint32, i64, ctypes.POINTER(ctypes.c_uint16)]),
+        "orc_div6_bits": (None, [ctypes.c_uint32, i64, f32p]),
+        "orc_recip_bits": (None, [ctypes.c_uint32, i64, f32p]),
         "orc_max_threads": (c_int, []),
         "orc_set_threads": (None, [c_int]),
     }
@@ -298,12 +305,60 @@ def quantize_dequantize(X, mode: int, amax, bound: float = 448.0):
 
 
 def to_bf16_bits(y: np.ndarray) -> np.ndarray:
-    """Round-to-nearest-even FP32 -> BF16 (as uint16 bit patterns), by torch's
-    conversion (a library routine standing in for the rounding step)."""
-    import torch
+    """Backward-overrides PR description (BF16 output of the dequantize): the
+    nearest BF16 value to each FP32 value, ties to the even pattern, as uint16
+    bit patterns (``orc_bf16_round`` in the C file)."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint16)
+    _load().orc_bf16_round_array(_p(y, ctypes.c_float), y.size, _p(out, ctypes.c_uint16))
+    return out
 
-    t = torch.from_numpy(np.ascontiguousarray(y, dtype=np.float32)).to(torch.bfloat16)
-    return t.view(torch.int16).numpy().view(np.uint16)
+
+# ------------------------------------------- runs of binary32 bit patterns
+# For exhaustive comparisons of hardware converters and arithmetic shortcuts
+# with the definitions: each returns the oracle's result for the patterns
+# start, start + 1, ..., start + n - 1 (start + n <= 2^32). Patterns outside
+# a function's domain carry a marker (see the C file) that callers mask out.
+def _check_run(start: int, n: int) -> None:
+    if not (0 <= start and n >= 0 and start + n <= 1 << 32):
+        raise ValueError("pattern run outside [0, 2^32)")
+
+
+def e2m1_encode_bits(start: int, n: int) -> np.ndarray:
+    _check_run(start, n)
+    out = np.empty(n, dtype=np.uint8)
+    _load().orc_e2m1_encode_bits(start, n, _p(out, ctypes.c_uint8))
+    return out
+
+
+def e4m3_encode_bits(start: int, n: int) -> np.ndarray:
+    _check_run(start, n)
+    out = np.empty(n, dtype=np.uint8)
+    _load().orc_e4m3_encode_bits(start, n, _p(out, ctypes.c_uint8))
+    return out
+
+
+def bf16_round_bits(start: int, n: int) -> np.ndarray:
+    _check_run(start, n)
+    out = np.empty(n, dtype=np.uint16)
+    _load().orc_bf16_round_bits(start, n, _p(out, ctypes.c_uint16))
+    return out
+
+
+def div6_bits(start: int, n: int) -> np.ndarray:
+    """RN(x / 6) (the block-scale step with top 6), as float32."""
+    _check_run(start, n)
+    out = np.empty(n, dtype=np.float32)
+    _load().orc_div6_bits(start, n, _p(out, ctypes.c_float))
+    return out
+
+
+def recip_bits(start: int, n: int) -> np.ndarray:
+    """min(RN(1 / D), FLT_MAX) for D > 0 (the encode-factor step), float32."""
+    _check_run(start, n)
+    out = np.empty(n, dtype=np.float32)
+    _load().orc_recip_bits(start, n, _p(out, ctypes.c_float))
+    return out
 
 
 # ------------------------------------------------------------ grouped tokens

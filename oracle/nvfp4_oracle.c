@@ -98,6 +98,14 @@ float orc_e4m3_value(int byte) {
   return (float)((byte & 0x80) ? -v : v);
 }
 
+/* The 127 finite non-negative E4M3 values by byte, filled from
+ * orc_e4m3_value once when the library is loaded (so the search below does
+ * not recompute them for every input). */
+static double E4M3_VALUES[0x7F];
+__attribute__((constructor)) static void fill_e4m3_values(void) {
+  for (int b = 0; b <= 0x7E; ++b) E4M3_VALUES[b] = (double)orc_e4m3_value(b);
+}
+
 /* Nearest of the 127 finite non-negative E4M3 values, ties to the even byte,
  * saturating at 448. s must be >= 0 (scales are magnitudes). s >= 448 is
  * decided first. Below it, for s >= 2^-21 the difference to any value (bits
@@ -109,7 +117,7 @@ uint8_t orc_e4m3_encode(float s) {
   int best = 0;
   double best_d = INFINITY;
   for (int b = 0; b <= 0x7E; ++b) {
-    double d = fabs((double)s - (double)orc_e4m3_value(b));
+    double d = fabs((double)s - E4M3_VALUES[b]);
     if (d < best_d || (d == best_d && (b & 1) == 0)) {
       best = b;
       best_d = d;
@@ -462,6 +470,108 @@ void orc_group_amax_expand(const float *ra, const int64_t *group_end, int64_t G,
       if (ra[i] > m) m = ra[i];
     for (int64_t i = start; i < group_end[g]; ++i) out[i] = m;
     start = group_end[g];
+  }
+}
+
+/* ---------------------------------------------------------------------------
+ * BF16 output of the dequantize ([P4] description: BF16 or FP32 output of the
+ * FP32 decode). Reading: the BF16 value nearest to the FP32 value, ties to the
+ * even bit pattern (round to nearest even), and past the largest finite BF16
+ * the rounding of an unbounded exponent, i.e. to infinity at or beyond the
+ * midpoint 2^128 - 2^119. The candidates are x with its low 16 bits cleared
+ * (the BF16 value next to x toward zero) and the next BF16 value away from
+ * zero; every distance below is exact in double (24-bit values within a
+ * factor of two of each other, or 2^128 against a value of exponent 127).
+ * NaN is outside the contract (a quiet NaN pattern is returned).
+ * ------------------------------------------------------------------------- */
+uint16_t orc_bf16_round(float x) {
+  uint32_t b;
+  memcpy(&b, &x, sizeof b);
+  if (isnan(x)) return (uint16_t)((b >> 16) | 0x0040u);
+  if (isinf(x)) return (uint16_t)(b >> 16);
+  const uint32_t lo = b & 0xFFFF0000u;
+  float flo;
+  memcpy(&flo, &lo, sizeof flo);
+  const double m_lo = fabs((double)flo);
+  /* magnitude one BF16 step up; from the largest finite BF16 that is 2^128 */
+  const uint32_t hi_mag = (lo & 0x7FFFFFFFu) + 0x00010000u;
+  double m_hi;
+  if (hi_mag >= 0x7F800000u) {
+    m_hi = ldexp(1.0, 128);
+  } else {
+    float fhi;
+    memcpy(&fhi, &hi_mag, sizeof fhi);
+    m_hi = (double)fhi;
+  }
+  const double m = fabs((double)x);
+  const double d_lo = m - m_lo, d_hi = m_hi - m;
+  const uint16_t p_lo = (uint16_t)(lo >> 16);
+  if (d_lo < d_hi) return p_lo;
+  if (d_lo > d_hi) return (uint16_t)(p_lo + 1u);
+  return (p_lo & 1u) ? (uint16_t)(p_lo + 1u) : p_lo;
+}
+
+void orc_bf16_round_array(const float *v, int64_t n, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(v[i]);
+}
+
+/* Forms over a run of binary32 bit patterns start, start + 1, ...
+ * (start + n <= 2^32), for exhaustive checks of hardware converters and
+ * arithmetic shortcuts against the definitions above. Patterns outside a
+ * function's domain get a marker the caller masks out: 0xFF for the element
+ * encoders (NaN input; negative input for E4M3), the pattern itself for the
+ * divisions (negative or NaN input). */
+static float bits_to_float(uint32_t u) {
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return f;
+}
+
+void orc_e2m1_encode_bits(uint32_t start, int64_t n, uint8_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const float v = bits_to_float(start + (uint32_t)i);
+    out[i] = isnan(v) ? 0xFF : orc_e2m1_encode(v);
+  }
+}
+
+void orc_e4m3_encode_bits(uint32_t start, int64_t n, uint8_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const float v = bits_to_float(start + (uint32_t)i);
+    out[i] = (isnan(v) || v < 0.0f || signbit(v)) ? 0xFF : orc_e4m3_encode(v);
+  }
+}
+
+void orc_bf16_round_bits(uint32_t start, int64_t n, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(bits_to_float(start + (uint32_t)i));
+}
+
+/* The block-scale divisions of the definition: RN(x / 6) (step s32 with the
+ * standard top 6) and the encode factor min(RN(1 / D), FLT_MAX) for D > 0. */
+void orc_div6_bits(uint32_t start, int64_t n, float *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const uint32_t u = start + (uint32_t)i;
+    const float x = bits_to_float(u);
+    out[i] = (isnan(x) || signbit(x)) ? x : x / 6.0f;
+  }
+}
+
+void orc_recip_bits(uint32_t start, int64_t n, float *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const uint32_t u = start + (uint32_t)i;
+    const float d = bits_to_float(u);
+    if (isnan(d) || signbit(d) || d == 0.0f) {
+      out[i] = d;
+    } else {
+      float r = 1.0f / d;
+      if (r > FLT_MAX) r = FLT_MAX;
+      out[i] = r;
+    }
   }
 }
 
