@@ -84,7 +84,9 @@ enum { NVFP4_FLAG_FORCE_TWO_KERNEL = 1u }; /* skip the fused amax kernel */
  * The fused pass runs only for BF16 input with M % 128 == 0, K % 128 == 0,
  * both row and column vectors requested, the flag clear and the environment
  * variable NVFP4_FUSED_AMAX not set to "0" (the gate and kill switch of the
- * fused-amax PR description). Both paths give identical bits (exact max). */
+ * fused-amax PR description). nvfp4_amax_rowcol also sends an X that is not
+ * 16-byte aligned to the separate kernels. Both paths give identical bits
+ * (exact max). */
 int nvfp4_amax_path(int in_dtype, int64_t M, int64_t K, int want_row, int want_col,
                     unsigned flags);
 
@@ -109,9 +111,27 @@ int nvfp4_amax_rowcol(const void* x, int in_dtype, int64_t M, int64_t K, float* 
  * group receives the max of the group's entries. group_end is a device int64
  * array [G], non-decreasing, last entry <= M; entries are clamped to [0, M]
  * on the device, so a bad array cannot cause an out-of-bounds access. Rows
- * past group_end[G-1] are left unchanged. G >= 1. */
+ * past group_end[G-1] are left unchanged. G >= 1, G <= 65535.
+ *   status  device int32 [1] or NULL. Non-NULL: the ends are validated on
+ *           the device first (the rules of nvfp4_check_group_end) and
+ *           *status receives 0 when they hold, else 1 + the first group
+ *           that breaks one; then row_amax is expanded only when *status is
+ *           0 and left unchanged otherwise (rejected without a host read).
+ *           NULL: no validation; misaligned groups still expand, but mode
+ *           ROWGROUP blocks that straddle two groups then mix their amaxes.
+ * The group ends stay on the device, so nothing synchronizes. */
 int nvfp4_group_amax_expand(float* row_amax, int64_t M, const int64_t* group_end, int64_t G,
-                            const float* noop, void* stream);
+                            int32_t* status, const float* noop, void* stream);
+
+/* Host-side validation of group ends the caller holds in host memory
+ * (row-scaled backward PR review, on the grouped GEMM's scale checks: a clear
+ * error rather than silently wrong results):
+ * returns NVFP4_OK when every entry lies in [0, M], the entries are
+ * non-decreasing and every entry other than M is a multiple of 16, so that
+ * no 1x16 block of the transposed copy straddles a group boundary in mode
+ * ROWGROUP; NVFP4_ERR_ARG otherwise (also for G < 1, G > 65535, M < 1 or a
+ * NULL pointer). Reads group_end [G] on the host; enqueues nothing. */
+int nvfp4_check_group_end(const int64_t* group_end, int64_t G, int64_t M);
 
 /* Quantize X into the rowwise copy, the columnwise (transposed) copy, or
  * both, in one pass over X (row-scaled backward PR summary: the columnwise

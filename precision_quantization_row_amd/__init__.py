@@ -39,6 +39,7 @@ NVFP4_FLAG_FORCE_TWO_KERNEL = 1
 
 # Every entry point include/nvfp4.h declares.
 EXPORTED = ("nvfp4_amax_path", "nvfp4_amax_rowcol", "nvfp4_group_amax_expand",
+            "nvfp4_check_group_end",
             "nvfp4_quantize_transpose", "nvfp4_quantize_4over6", "nvfp4_quantize_2d",
             "nvfp4_quantize_grouped",
             "nvfp4_quantize_dequantize", "nvfp4_dequantize",
@@ -74,7 +75,9 @@ def load_library():
     lib.nvfp4_amax_rowcol.restype = c_int
     lib.nvfp4_amax_rowcol.argtypes = [vp, c_int, i64, i64, f32p, f32p, f32p, f32p, c_uint, vp]
     lib.nvfp4_group_amax_expand.restype = c_int
-    lib.nvfp4_group_amax_expand.argtypes = [f32p, i64, i64p, i64, f32p, vp]
+    lib.nvfp4_group_amax_expand.argtypes = [f32p, i64, i64p, i64, vp, f32p, vp]
+    lib.nvfp4_check_group_end.restype = c_int
+    lib.nvfp4_check_group_end.argtypes = [i64p, i64, i64]
     lib.nvfp4_quantize_transpose.restype = c_int
     lib.nvfp4_quantize_transpose.argtypes = [vp, c_int, i64, i64, c_int, f32p, c_int, f32p, c_f,
                                              u8p, u8p, u8p, u8p, f32p, vp]
@@ -176,15 +179,36 @@ def nvfp4_amax_rowcol(x: torch.Tensor, row_amax: Optional[torch.Tensor] = None,
     _check("nvfp4_amax_rowcol", st)
 
 
+def nvfp4_check_group_end(group_end: torch.Tensor, M: int) -> int:
+    """Host-side validation of group ends held in host memory (int64 CPU
+    tensor); returns the C status (NVFP4_OK or NVFP4_ERR_ARG)."""
+    if not isinstance(group_end, torch.Tensor) or group_end.is_cuda:
+        raise ValueError("group_end must be a host (CPU) tensor")
+    if group_end.dtype != torch.int64 or not group_end.is_contiguous():
+        raise TypeError("group_end must be a contiguous int64 tensor")
+    return int(load_library().nvfp4_check_group_end(ctypes.c_void_p(group_end.data_ptr()),
+                                                    group_end.numel(), int(M)))
+
+
 def nvfp4_group_amax_expand(row_amax: torch.Tensor, group_end: torch.Tensor,
+                            status: Optional[torch.Tensor] = None,
                             noop: Optional[torch.Tensor] = None, stream=None) -> None:
+    """group_end: an int64 device tensor (validated on the device when a
+    status [1] int32 device tensor is given), or an int64 CPU tensor, which
+    is validated on the host (Nvfp4Error with NVFP4_ERR_ARG when a group
+    boundary is misaligned) and then copied to the device."""
     lib = load_library()
     _dev(row_amax, "row_amax", _F32)
     dev = row_amax.device
+    if isinstance(group_end, torch.Tensor) and not group_end.is_cuda:
+        _check("nvfp4_check_group_end", nvfp4_check_group_end(group_end, row_amax.numel()))
+        group_end = group_end.to(dev)
     _dev(group_end, "group_end", (torch.int64,), None, dev)
+    _dev(status, "status", (torch.int32,), 1, dev)
     _dev(noop, "noop", _F32, 1, dev)
     st = lib.nvfp4_group_amax_expand(_ptr(row_amax), row_amax.numel(), _ptr(group_end),
-                                     group_end.numel(), _ptr(noop), _stream(stream, dev))
+                                     group_end.numel(), _ptr(status), _ptr(noop),
+                                     _stream(stream, dev))
     _check("nvfp4_group_amax_expand", st)
 
 

@@ -351,10 +351,40 @@ __global__ void __launch_bounds__(TENSOR_THREADS) tensor_amax_kernel(const T* __
 // ----------------------------------------------------- group expansion
 // One workgroup per group: max over the group's rows, then every row of the
 // group receives it. Groups are disjoint, so the in-place update is safe.
+// Validity of the group ends for the transposed copy's per-group blocks:
+// every entry within [0, M], non-decreasing, and a multiple of 16 unless it
+// equals M (a 1x16 column block must not straddle a group boundary). One
+// workgroup; *status = 0 when valid, else 1 + the first g whose end breaks a
+// rule.
+__global__ void __launch_bounds__(256) group_check_kernel(const int64_t* __restrict__ group_end,
+                                                          int64_t G, int64_t M, int32_t* status,
+                                                          const float* noop) {
+  if (skip(noop)) return;
+  __shared__ int64_t first[4];
+  int64_t bad = G;  // smallest bad g seen by this thread (G: none)
+  for (int64_t g = threadIdx.x; g < G && g < bad; g += 256) {
+    const int64_t e = group_end[g];
+    const int64_t b = g == 0 ? 0 : group_end[g - 1];
+    if (e < 0 || e > M || e < b || (e != M && e % 16 != 0)) bad = g;
+  }
+  for (int off = 32; off > 0; off >>= 1) bad = min(bad, (int64_t)__shfl_xor(bad, off));
+  if ((threadIdx.x & 63) == 0) first[threadIdx.x >> 6] = bad;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int64_t f = min(min(first[0], first[1]), min(first[2], first[3]));
+    *status = f < G ? (int32_t)min(f + 1, (int64_t)0x7FFFFFFF) : 0;
+  }
+}
+
+// status == nullptr: expand whatever the ends are (clamped); otherwise only
+// when group_check_kernel found them valid, so misaligned groups leave ra
+// unchanged.
 __global__ void __launch_bounds__(256) group_expand_kernel(float* __restrict__ ra, int64_t M,
                                                            const int64_t* __restrict__ group_end,
+                                                           const int32_t* status,
                                                            const float* noop) {
   if (skip(noop)) return;
+  if (status != nullptr && *status != 0) return;
   __shared__ uint32_t red[4];
   const int64_t g = blockIdx.x;
   int64_t s = g == 0 ? 0 : group_end[g - 1];
@@ -539,8 +569,13 @@ int launch_tensor_amax(const void* x, int in_dtype, int64_t n, float* ta, const 
 }
 
 int launch_group_expand(float* ra, int64_t M, const int64_t* group_end, int64_t G,
-                        const float* noop, hipStream_t s) {
-  hipLaunchKernelGGL(group_expand_kernel, dim3((unsigned)G), dim3(256), 0, s, ra, M, group_end, noop);
+                        int32_t* status, const float* noop, hipStream_t s) {
+  if (status != nullptr) {
+    hipLaunchKernelGGL(group_check_kernel, dim3(1), dim3(256), 0, s, group_end, G, M, status, noop);
+    if (hipGetLastError() != hipSuccess) return -3;
+  }
+  hipLaunchKernelGGL(group_expand_kernel, dim3((unsigned)G), dim3(256), 0, s, ra, M, group_end,
+                     status, noop);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -368,14 +368,11 @@ __device__ __forceinline__ Cand cand_scale(float bamax, float top, float a, floa
 }
 
 // Sum over 8 elements, in order, of (x_k - RN(e2m1(code_k) * d))^2 in
-// binary64; code k is nibble k of word (v_cvt_scalef32_pk_f32_fp4 with scale
-// 1.0 decodes it exactly).
+// binary64; code k is nibble k of word (decoded exactly by fp4x2_decode).
 __device__ __forceinline__ double sq_error8(const float (&x)[8], uint32_t word, float d) {
   float v[8];
-  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
-  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
-  const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
-  const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+  const f32x2 p0 = fp4x2_decode<0>(word), p1 = fp4x2_decode<1>(word);
+  const f32x2 p2 = fp4x2_decode<2>(word), p3 = fp4x2_decode<3>(word);
   v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
   v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
   double s = 0.0;
@@ -613,7 +610,7 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
     else
       return cm[k];
   };
-  uint32_t bmin = 0xFFFFFFFFu, dmin = 0xFFFFFFFFu, dmax = 0u;
+  uint32_t bmin = 0xFFFFFFFFu, dmin = 0xFFFFFFFFu, dmax = 0u, dsig = 0u;
   if constexpr (ROWW) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -634,6 +631,7 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
       bmin = min(bmin, bsel[j]);
       dmin = min(dmin, db);
       dmax = max(dmax, db);
+      dsig = max(dsig, db & kSigMask);
     }
   }
   if constexpr (COLW) {
@@ -646,10 +644,13 @@ __device__ __forceinline__ void process_block_batched(const uint32_t (&w)[16][Bl
       bmin = min(bmin, col_bits(k));
       dmin = min(dmin, db);
       dmax = max(dmax, db);
+      dsig = max(dsig, db & kSigMask);
     }
   }
-  // the fast forms hold for bamax >= 2^-125 and D in [2^-126, 2^126)
-  const bool ok = (bmin >= kFastBamaxMin) & (dmin >= 0x00800000u) & (dmax < 0x7E800000u);
+  // the fast forms hold for bamax >= 2^-121 and D in [2^-126, 2^126) whose
+  // significand is not all ones (recip_fast_ok for every block)
+  const bool ok = (bmin >= kFastBamaxMin) & (dmin >= 0x00800000u) & (dmax < 0x7E800000u) &
+                  (dsig != kSigMask);
   if (!ok) {
     // The block maxima pass through an empty asm statement so that the
     // compiler cannot share work between the two forms: sharing would keep

@@ -19,27 +19,6 @@
 
 namespace nvfp4 {
 
-// E4M3 byte -> float, exact. Low 7 bits: exponent field e, mantissa m;
-// e == 0: m * 2^-9, else (1 + m/8) * 2^(e-7) = fp32 pattern (byte + (120<<3)) << 20.
-__device__ __forceinline__ float e4m3_value(uint32_t byte) {
-  const uint32_t mag = byte & 0x7Fu;
-  const float v = mag < 8u ? (float)mag * 0x1p-9f : __uint_as_float((mag + (120u << 3)) << 20);
-  return (byte & 0x80u) ? -v : v;
-}
-
-// E2M1 code -> float, exact: magnitude field e = (c >> 1) & 3, mantissa m = c & 1;
-// e == 0: 0.5 m; else fp32 pattern ((e + 126) << 23) | (m << 22). Bit 3 = sign.
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  const uint32_t mag = e == 0u ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
-  return __uint_as_float(mag | ((c & 8u) << 28));
-}
-
-__device__ __forceinline__ uint32_t bf16_rne(float y) {
-  const uint32_t b = __float_as_uint(y);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
-}
-
 template <bool OUT_BF16>
 __global__ void __launch_bounds__(256) dequant_kernel(const DequantArgs p, int64_t nb, int vec) {
   if (p.noop != nullptr && *p.noop == 1.0f) return;
@@ -99,24 +78,7 @@ __global__ void __launch_bounds__(256) dequant_kernel(const DequantArgs p, int64
   }
 }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Two E2M1 codes (byte SEL of w: low nibble first) -> two floats, exact
-// (v_cvt_scalef32_pk_f32_fp4 with scale 1.0 equals the E2M1 table for all 256
-// bytes and all four selects, checked on gfx950).
-template <int SEL>
-__device__ __forceinline__ f32x2 fp4x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-}
-
-// Two floats -> two BF16 (round to nearest even; v_cvt_pk_bf16_f32 equals
-// the RNE definition for every non-NaN fp32, checked on gfx950).
-__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // Vector path: C % 16 == 0, code rows 4-byte aligned, output rows 16-byte
 // aligned. A lane decodes EPL consecutive elements of one line (8 for BF16
@@ -142,13 +104,14 @@ __global__ void __launch_bounds__(256) dequant_vec_kernel(const DequantArgs p, i
     const uint8_t* qp = p.q + r * qrs + c / 2;
     if constexpr (OUT_BF16) {
       const uint32_t w = *reinterpret_cast<const uint32_t*>(qp);
-      const f32x2 v0 = fp4x2<0>(w), v1 = fp4x2<1>(w), v2 = fp4x2<2>(w), v3 = fp4x2<3>(w);
+      const f32x2 v0 = fp4x2_decode<0>(w), v1 = fp4x2_decode<1>(w);
+      const f32x2 v2 = fp4x2_decode<2>(w), v3 = fp4x2_decode<3>(w);
       const u32x4 o = {bf16x2_rne(v0.x * d, v0.y * d), bf16x2_rne(v1.x * d, v1.y * d),
                        bf16x2_rne(v2.x * d, v2.y * d), bf16x2_rne(v3.x * d, v3.y * d)};
       __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.y) + r * C + c));
     } else {
       const uint32_t w = *reinterpret_cast<const uint16_t*>(qp);
-      const f32x2 v0 = fp4x2<0>(w), v1 = fp4x2<1>(w);
+      const f32x2 v0 = fp4x2_decode<0>(w), v1 = fp4x2_decode<1>(w);
       const u32x4 o = {__float_as_uint(v0.x * d), __float_as_uint(v0.y * d),
                        __float_as_uint(v1.x * d), __float_as_uint(v1.y * d)};
       __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<float*>(p.y) + r * C + c));

@@ -72,7 +72,11 @@ int nvfp4_amax_rowcol(const void* x, int in_dtype, int64_t M, int64_t K, float* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   int rc = launch_amax_init(row_amax, M, col_amax, K, tensor_amax, noop, s);
   if (rc) return NVFP4_ERR_HIP;
-  const int path = nvfp4_amax_path(in_dtype, M, K, row_amax != nullptr, col_amax != nullptr, flags);
+  int path = nvfp4_amax_path(in_dtype, M, K, row_amax != nullptr, col_amax != nullptr, flags);
+  // the fused pass reads 16-byte vectors: an X that is not 16-byte aligned
+  // (a view with a storage offset) takes the two-kernel path, which checks
+  // alignment itself
+  if (path == 1 && (reinterpret_cast<uintptr_t>(x) & 15) != 0) path = 2;
   if (path == 1)
     rc = launch_fused_amax_bf16(x, M, K, row_amax, col_amax, noop, s);
   else if (path == 2)
@@ -86,11 +90,23 @@ int nvfp4_amax_rowcol(const void* x, int in_dtype, int64_t M, int64_t K, float* 
 }
 
 int nvfp4_group_amax_expand(float* row_amax, int64_t M, const int64_t* group_end, int64_t G,
-                            const float* noop, void* stream) {
+                            int32_t* status, const float* noop, void* stream) {
   if (row_amax == nullptr || group_end == nullptr || M < 1 || G < 1 || G > 65535) return NVFP4_ERR_ARG;
-  return launch_group_expand(row_amax, M, group_end, G, noop, static_cast<hipStream_t>(stream))
+  return launch_group_expand(row_amax, M, group_end, G, status, noop,
+                             static_cast<hipStream_t>(stream))
              ? NVFP4_ERR_HIP
              : NVFP4_OK;
+}
+
+int nvfp4_check_group_end(const int64_t* group_end, int64_t G, int64_t M) {
+  if (group_end == nullptr || M < 1 || G < 1 || G > 65535) return NVFP4_ERR_ARG;
+  int64_t b = 0;
+  for (int64_t g = 0; g < G; ++g) {
+    const int64_t e = group_end[g];
+    if (e < 0 || e > M || e < b || (e != M && e % 16 != 0)) return NVFP4_ERR_ARG;
+    b = e;
+  }
+  return NVFP4_OK;
 }
 
 static int quantize_impl(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,

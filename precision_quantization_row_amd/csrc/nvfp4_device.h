@@ -68,16 +68,33 @@ __device__ __forceinline__ float div6_rn(float x) {
   return x / kE2M1Max;
 }
 
+// Significand field of a binary32 pattern that is all ones: d = (2 - 2^-23) 2^k.
+constexpr uint32_t kSigMask = 0x007FFFFFu;
+
 // min(RN(1 / d), FLT_MAX) for d > 0. For d in [2^-126, 2^126) the hardware
-// reciprocal is within an ulp and one Newton step fma(fma(-d, r, 1), r, r)
-// lands on the correctly rounded value (checked exhaustively on gfx950 for
-// every d in that range); other d take the IEEE division.
+// reciprocal r is within an ulp of 1/d, and one Newton step
+// fma(fma(-d, r, 1), r, r) gives RN(1/d) from either neighbour of 1/d except
+// at one significand: for d = (2 - 2^-23) 2^k, 1/d lies 2^-48 relative above
+// the midpoint between 2^-k-1 and its successor, and from r = 2^-k-1 the
+// step computes exactly that midpoint, which rounds to even (the wrong side).
+// Those d, and d outside the range, take the IEEE division, so the result
+// never depends on which neighbour the hardware returns (the exception and
+// the exactness elsewhere are shown by exact rational arithmetic over every
+// significand, from both neighbours).
+__device__ __forceinline__ float recip_newton(float d) {
+  const float r = __builtin_amdgcn_rcpf(d);
+  return __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+}
 __device__ __forceinline__ float recip_rn(float d) {
-  if (d >= 0x1p-126f && d < 0x1p126f) {
-    const float r = __builtin_amdgcn_rcpf(d);
-    return __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
-  }
+  if (d >= 0x1p-126f && d < 0x1p126f && (__float_as_uint(d) & kSigMask) != kSigMask)
+    return recip_newton(d);
   return fminf(1.0f / d, kFltMax);
+}
+
+// The fast reciprocal form holds for this decode-scale bit pattern: D in
+// [2^-126, 2^126) and a significand that is not all ones.
+__device__ __forceinline__ bool recip_fast_ok(uint32_t db) {
+  return ((db - 0x00800000u) < 0x7E000000u) & ((db & kSigMask) != kSigMask);
 }
 
 // One block: from its max magnitude, the line amax a, the line's S_enc and
@@ -99,8 +116,9 @@ __device__ __forceinline__ void block_scale(float bamax, float a, float s_enc, f
 }
 
 // The unguarded scale chain itself: *byte (low byte) and *enc as block_scale
-// gives them whenever bamax >= 2^-121 and D lies in [2^-126, 2^126); returns
-// D's bit pattern so that callers can check that range for many blocks at once.
+// gives them whenever bamax >= 2^-121 and recip_fast_ok(D) holds; returns D's
+// bit pattern so that callers can check those conditions for many blocks at
+// once.
 // RN(bamax / 6) is fma(bamax, H, RN(bamax * L)) with H = RN(1/6) and
 // L = RN(1/6 - H): bamax / 6 is never closer to a rounding midpoint than a
 // sixth of an ulp, far more than this two-term product's error, and the
@@ -109,31 +127,32 @@ __device__ __forceinline__ void block_scale(float bamax, float a, float s_enc, f
 // the upper half of its first operand's register, so it starts from s32's
 // own bits (no zeroing move); only the low byte is used.
 constexpr uint32_t kFastBamaxMin = 0x03000000u;  // bit pattern of 2^-121
-__device__ __forceinline__ uint32_t block_scale_unchecked(float bamax, float a, float s_enc,
-                                                          float f_inv, uint32_t* byte, float* enc) {
+__device__ __forceinline__ float div6_two_term(float x) {
   constexpr float kR6 = 0.16666667163372039794921875f;  // RN(1/6)
   constexpr float kR6lo = -0x1.555556p-28f;              // RN(1/6 - RN(1/6))
-  const float q = __builtin_fmaf(bamax, kR6, bamax * kR6lo);
-  const float s32 = fminf(q * s_enc, kE4M3Max);
+  return __builtin_fmaf(x, kR6, x * kR6lo);
+}
+__device__ __forceinline__ uint32_t block_scale_unchecked(float bamax, float a, float s_enc,
+                                                          float f_inv, uint32_t* byte, float* enc) {
+  const float s32 = fminf(div6_two_term(bamax) * s_enc, kE4M3Max);
   const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(s32, s32, __float_as_int(s32), false);
   *byte = (uint32_t)pk;
   const float sq = __builtin_amdgcn_cvt_f32_fp8(pk, 0);
   const float d = (sq * a) * f_inv;
-  const float r = __builtin_amdgcn_rcpf(d);
-  *enc = __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+  *enc = recip_newton(d);
   return __float_as_uint(d);
 }
 
-// block_scale without its range guards, for the batched block code: the same
-// results whenever bamax >= 2^-121 (the two-term quotient above) and D lies in
-// [2^-126, 2^126) (recip_rn's fast form; then D != 0 too), which it reports.
-// *byte is the converter's packed result: its low byte is the scale byte.
-// Callers redo the lanes where it returns false with block_scale.
+// block_scale without its range guards: the same results whenever
+// bamax >= 2^-121 (the two-term quotient above) and recip_fast_ok(D) (then
+// D != 0 too), which it reports. *byte is the converter's packed result: its
+// low byte is the scale byte. Callers redo the lanes where it returns false
+// with block_scale.
 __device__ __forceinline__ bool block_scale_fast(float bamax, float a, float s_enc, float f_inv,
                                                  uint32_t* byte, float* enc) {
   const uint32_t db = block_scale_unchecked(bamax, a, s_enc, f_inv, byte, enc);
   const uint32_t bb = __float_as_uint(bamax);
-  return (bb >= kFastBamaxMin) & ((db - 0x00800000u) < 0x7E000000u);
+  return (bb >= kFastBamaxMin) & recip_fast_ok(db);
 }
 
 // block_scale that also returns the block's decode scale D (the factor the
@@ -169,6 +188,49 @@ __device__ __forceinline__ uint32_t e2m1_pack8(float v0, float v1, float v2, flo
   w = NVFP4_CVT_FP4X2(w, v4, v5, 2);
   w = NVFP4_CVT_FP4X2(w, v6, v7, 3);
   return w;
+}
+
+// ------------------------------------------------------------ decoding
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two E2M1 codes (byte SEL of w, low nibble first) -> two floats, exact:
+// v_cvt_scalef32_pk_f32_fp4 with scale 1.0 equals the E2M1 table for every
+// byte and select (checked exhaustively on gfx950).
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4x2_decode(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// Two floats -> two BF16 (element 0 in the low half), round to nearest even:
+// v_cvt_pk_bf16_f32 equals the RNE definition for every non-NaN fp32
+// (checked exhaustively on gfx950).
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// One float -> BF16 bits, round to nearest even, in integer arithmetic (the
+// carry into bit 16 is the rounding; ties keep an even bit 16). Non-NaN input.
+__device__ __forceinline__ uint32_t bf16_rne(float y) {
+  const uint32_t b = __float_as_uint(y);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// E4M3 byte -> float, exact. Low 7 bits: exponent field e, mantissa m;
+// e == 0: m * 2^-9, else (1 + m/8) * 2^(e-7) = fp32 pattern (byte + (120<<3)) << 20.
+__device__ __forceinline__ float e4m3_value(uint32_t byte) {
+  const uint32_t mag = byte & 0x7Fu;
+  const float v = mag < 8u ? (float)mag * 0x1p-9f : __uint_as_float((mag + (120u << 3)) << 20);
+  return (byte & 0x80u) ? -v : v;
+}
+
+// E2M1 code -> float, exact: magnitude field e = (c >> 1) & 3, mantissa m = c & 1;
+// e == 0: 0.5 m; else fp32 pattern ((e + 126) << 23) | (m << 22). Bit 3 = sign.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const uint32_t mag = e == 0u ? (m ? 0x3F000000u : 0u) : (((e + 126u) << 23) | (m << 22));
+  return __uint_as_float(mag | ((c & 8u) << 28));
 }
 
 // -------------------------------------------------------- grouped tokens

@@ -20,7 +20,7 @@ int launch_row_col_amax(const void* x, int in_dtype, int64_t M, int64_t K, float
 int launch_tensor_amax(const void* x, int in_dtype, int64_t n, float* ta, const float* noop,
                        hipStream_t s);
 int launch_group_expand(float* ra, int64_t M, const int64_t* group_end, int64_t G,
-                        const float* noop, hipStream_t s);
+                        int32_t* status, const float* noop, hipStream_t s);
 // grouped tokens: the group amax of each token group over the group's padded
 // rows, 0 past the last group; every row of ra [M_out] is written
 int launch_grouped_amax(const void* x, int in_dtype, int64_t T, int64_t K, const int64_t* grows,

@@ -18,24 +18,7 @@
 
 namespace nvfp4 {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Two E2M1 codes (byte SEL of w, low nibble first) -> two floats, exact
-// (v_cvt_scalef32_pk_f32_fp4 with scale 1.0 equals the E2M1 table for every
-// byte and select, checked on gfx950).
-template <int SEL>
-__device__ __forceinline__ f32x2 qdq_fp4x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-}
-
-// Two floats -> two BF16, round to nearest even (v_cvt_pk_bf16_f32, equal to
-// the RNE definition for every non-NaN fp32, checked on gfx950).
-__device__ __forceinline__ uint32_t qdq_bf16x2(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // Vector path: K % 16 == 0 and aligned rows (x and y 16 bytes, codes 4
 // bytes). Workgroup tiles are (row, chunk of 256 x 8 columns); lane t of a
@@ -89,11 +72,11 @@ __global__ void __launch_bounds__(256) qdq_vec_kernel(const QdqArgs p, int64_t n
       *reinterpret_cast<uint32_t*>(p.q + r * qrs + c / 2) = code;
       if (par == 0) p.sc[r * srs + c / 16] = (uint8_t)byte;
     }
-    const f32x2 y0 = qdq_fp4x2<0>(code), y1 = qdq_fp4x2<1>(code);
-    const f32x2 y2 = qdq_fp4x2<2>(code), y3 = qdq_fp4x2<3>(code);
+    const f32x2 y0 = fp4x2_decode<0>(code), y1 = fp4x2_decode<1>(code);
+    const f32x2 y2 = fp4x2_decode<2>(code), y3 = fp4x2_decode<3>(code);
     if constexpr (OUT_BF16) {
-      const u32x4 o = {qdq_bf16x2(y0.x * dec, y0.y * dec), qdq_bf16x2(y1.x * dec, y1.y * dec),
-                       qdq_bf16x2(y2.x * dec, y2.y * dec), qdq_bf16x2(y3.x * dec, y3.y * dec)};
+      const u32x4 o = {bf16x2_rne(y0.x * dec, y0.y * dec), bf16x2_rne(y1.x * dec, y1.y * dec),
+                       bf16x2_rne(y2.x * dec, y2.y * dec), bf16x2_rne(y3.x * dec, y3.y * dec)};
       __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(p.y) + r * K + c));
     } else {
       u32x4* dst = reinterpret_cast<u32x4*>(static_cast<float*>(p.y) + r * K + c);
@@ -154,10 +137,10 @@ __global__ void __launch_bounds__(256) qdq_kernel(const QdqArgs p) {
       const uint32_t w = j < 4 ? w0 : w1;
       f32x2 e;
       switch (j & 3) {
-        case 0: e = qdq_fp4x2<0>(w); break;
-        case 1: e = qdq_fp4x2<1>(w); break;
-        case 2: e = qdq_fp4x2<2>(w); break;
-        default: e = qdq_fp4x2<3>(w); break;
+        case 0: e = fp4x2_decode<0>(w); break;
+        case 1: e = fp4x2_decode<1>(w); break;
+        case 2: e = fp4x2_decode<2>(w); break;
+        default: e = fp4x2_decode<3>(w); break;
       }
       const float ya = e.x * dec, yb = e.y * dec;
       for (int h = 0; h < 2; ++h) {

@@ -132,8 +132,31 @@ def test_validation_rejects_before_launch():
     assert g(T=1 << 31) == p.NVFP4_ERR_UNSUPPORTED
     assert g(M=(1 << 31) - 1) == p.NVFP4_ERR_UNSUPPORTED
     # group expansion
-    assert lib.nvfp4_group_amax_expand(_fake(), 16, _fake(), 0, None, None) == E
-    assert lib.nvfp4_group_amax_expand(None, 16, _fake(), 2, None, None) == E
+    assert lib.nvfp4_group_amax_expand(_fake(), 16, _fake(), 0, None, None, None) == E
+    assert lib.nvfp4_group_amax_expand(None, 16, _fake(), 2, None, None, None) == E
+
+
+def test_host_group_end_check():
+    """Group ends held on the host are validated before anything is enqueued:
+    in [0, M], non-decreasing, and a multiple of 16 unless equal to M (so no
+    1x16 block of the transposed copy straddles a group boundary in mode
+    ROWGROUP; row-scaled backward PR review: a clear error rather than
+    silently wrong results)."""
+    import torch
+    ok, E = p.NVFP4_OK, p.NVFP4_ERR_ARG
+    chk = lambda ends, M: p.nvfp4_check_group_end(torch.tensor(ends, dtype=torch.int64), M)
+    assert chk([16, 32, 100], 100) == ok      # last end == M need not be aligned
+    assert chk([0, 0, 48, 48], 64) == ok      # empty groups
+    assert chk([64], 64) == ok
+    assert chk([16, 40, 100], 100) == E       # group 2 starts at row 40
+    assert chk([17], 64) == E                 # last end short of M, not aligned
+    assert chk([32, 16], 64) == E             # decreasing
+    assert chk([-16, 32], 64) == E
+    assert chk([16, 80], 64) == E             # past M
+    assert p.load_library().nvfp4_check_group_end(None, 2, 64) == E
+    assert chk([16], 0) == E
+    with pytest.raises(TypeError):
+        p.nvfp4_check_group_end(torch.tensor([16], dtype=torch.int32), 16)
 
 
 def test_binding_rejects_host_tensors():

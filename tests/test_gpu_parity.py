@@ -83,8 +83,9 @@ def test_interior_half_macro_tiles(M, K):
 
 
 def test_fused_equals_two_kernel_bytes():
-    """Fused-amax PR description: the fused pass is an exact max, so its
-    results are byte-identical to the two-kernel path."""
+    """Fused-amax PR, description: an exact max does not depend on the
+    order of evaluation, so the one-pass and the two-kernel amax must agree
+    in every bit."""
     w = workloads.make("llm_mlp", (1024, 2048))
     x = w.x.to(DEV)
     assert p.nvfp4_amax_path(p.NVFP4_BF16, 1024, 2048, 1, 1, 0) == 1
@@ -92,6 +93,26 @@ def test_fused_equals_two_kernel_bytes():
     ra2, ca2, _ = gpu_amax(x, flags=p.NVFP4_FLAG_FORCE_TWO_KERNEL)
     assert_same("row", f32_bits(ra1), f32_bits(ra2))
     assert_same("col", f32_bits(ca1), f32_bits(ca2))
+
+
+@pytest.mark.parametrize("M,K", [(256, 512), (1024, 2048)])
+def test_misaligned_x_takes_the_two_kernel_amax(M, K):
+    """A BF16 view two bytes past a 16-byte boundary: the fused pass reads
+    16-byte vectors, so the call sends it to the two-kernel path, with the
+    oracle's bits either way."""
+    w = workloads.make("llm_mlp", (M, K))
+    base = torch.empty(M * K + 8, dtype=torch.bfloat16, device=DEV)
+    x = base[1:1 + M * K].view(M, K)
+    x.copy_(w.x.to(DEV))
+    assert x.data_ptr() % 16 == 2 and x.is_contiguous()
+    xf = w.x.float().numpy()
+    ra, ca, _ = gpu_amax(x)
+    assert_same("row", f32_bits(ra), oracle.amax_rows(xf).view(np.uint32))
+    assert_same("col", f32_bits(ca), oracle.amax_cols(xf).view(np.uint32))
+    out = gpu_quantize(x, 1, ra, 1, ca, 448.0)
+    qr, sr = oracle.quantize_rowwise(xf, oracle.MODE_LINE, oracle.amax_rows(xf), 448.0)
+    assert_same("q_row", to_np(out["q_row"]), qr)
+    assert_same("s_row", to_np(out["s_row"]), sr)
 
 
 def test_tensor_amax_and_per_tensor_quantize():
@@ -237,6 +258,47 @@ def test_group_expand_matches_oracle():
     p.nvfp4_group_amax_expand(r, ge.to(DEV))
     want = oracle.group_amax_expand(ra.numpy(), ge.numpy())
     assert_same("expanded", f32_bits(r), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("ends,first_bad", [
+    ([0, 128, 128, 384, 1000], 0),       # valid: the last end (M) need not be aligned
+    ([16, 40, 1000], 2),                 # group 1 ends (group 2 starts) at row 40
+    ([128, 64, 1000], 2),                # decreasing
+    ([128, 1001], 2),                    # past M
+    ([-16, 1000], 1),
+    ([992], 0),                          # rows past the last group: allowed when aligned
+    ([995], 1),                          # ... not when the last end is not a multiple of 16
+])
+def test_group_expand_validates_on_device(ends, first_bad):
+    """With a status buffer the ends are checked on the device: status 0 and
+    the expansion when every end lies in [0, M], in order, and is a multiple
+    of 16 unless it equals M; otherwise 1 + the first offending group and
+    row_amax untouched (the host reads nothing: the caller reads status)."""
+    g = torch.Generator().manual_seed(5)
+    ra = torch.rand(1000, generator=g) * 10
+    r = ra.to(DEV)
+    ge = torch.tensor(ends, dtype=torch.int64)
+    st = torch.full((1,), -5, dtype=torch.int32, device=DEV)
+    p.nvfp4_group_amax_expand(r, ge.to(DEV), status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == first_bad
+    if first_bad == 0:
+        want = oracle.group_amax_expand(ra.numpy(), ge.numpy())
+        assert_same("expanded", f32_bits(r), want.view(np.uint32))
+        # the host-held form of the same ends passes the host check and expands
+        r2 = ra.to(DEV)
+        p.nvfp4_group_amax_expand(r2, ge)
+        assert_same("expanded (host ends)", f32_bits(r2), want.view(np.uint32))
+    else:
+        assert torch.equal(r.cpu(), ra)
+        with pytest.raises(p.Nvfp4Error):
+            p.nvfp4_group_amax_expand(ra.to(DEV), ge)  # host ends: rejected before any launch
+    # noop = 1: neither the status nor the amax vector is written
+    st.fill_(-5)
+    r3 = ra.to(DEV)
+    p.nvfp4_group_amax_expand(r3, ge.to(DEV), status=st, noop=torch.ones(1, device=DEV))
+    torch.cuda.synchronize()
+    assert int(st.item()) == -5 and torch.equal(r3.cpu(), ra)
 
 
 def test_other_stream():

@@ -185,9 +185,9 @@ def test_grid_values_round_trip_exactly(k):
 
 # ------------------------------------------------- grouped tokens (MoE) invariants
 def test_group_expanded_quantize_equals_per_split():
-    """torchao grouped-GEMM PR description: the group amaxes expand to a
-    per-row amax vector so that one quantize call is bitwise identical to
-    quantizing each split separately; padded rows quantize to zero codes."""
+    """torchao grouped-GEMM PR, description: with each group's amax spread
+    over its rows, a single call over all groups must give the same bytes as
+    separate calls per group, and the zero padding rows give zero codes."""
     w = workloads.moe_groups((700, 64), n_groups=5, align=32)
     x = _f32(w.x)
     M, K = x.shape
