@@ -22,8 +22,10 @@ the whole region before the GPU reaches it. Also reported: the dequantize
 kernel's bandwidth, the other kernels of the path on the workloads they serve
 (two-kernel and per-tensor amax, 2-D tiles, four-over-six, quantize +
 dequantize, the FP32 edge matrix, grouped tokens, and the two small matrices
-cold), and the CPU oracle timed on a bounded sample of the same workload on
-the host cores.
+cold and warm), the fused-amax PR's comparison (whole quantize with the fused
+amax against the separate row and column amax kernels, medians), what plain
+streaming kernels sustain on the same GPU (read, write, copy), and the CPU
+oracle timed on a bounded sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration   (plain torch copy, for counter scaling)
@@ -69,13 +71,133 @@ def measured_traffic():
     return rec.get("cast_hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+class StreamRef:
+    """Plain streaming kernels (16-byte non-temporal loads / stores, nothing
+    else per byte) from bench_ref/libstream_ref.so: the HBM ceiling the
+    quantize path is set against, and a read-only pass that evicts the
+    memory-side cache between cold repetitions without leaving dirty lines
+    behind (a fill would leave its writes to drain into the timed call)."""
+
+    def __init__(self, torch, dev):
+        import ctypes
+
+        from precision_quantization_row_amd.build import stream_ref_path
+
+        self.torch, self.dev, self.ct = torch, dev, ctypes
+        lib = ctypes.CDLL(stream_ref_path())
+        vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        for name, args in (("stream_read", [vp, i64, vp, c_int, c_int, vp]),
+                           ("stream_write", [vp, i64, c_int, vp]),
+                           ("stream_copy", [vp, vp, i64, c_int, vp])):
+            fn = getattr(lib, name)
+            fn.restype = c_int
+            fn.argtypes = args
+        self.lib = lib
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        self.flush_buf = None
+
+    def _st(self):
+        return self.ct.c_void_p(self.torch.cuda.current_stream(self.dev).cuda_stream)
+
+    def read(self, t, grid=4096, cached=False):
+        assert self.lib.stream_read(t.data_ptr(), t.numel() * t.element_size(),
+                                    self.sink.data_ptr(), grid, int(cached), self._st()) == 0
+
+    def write(self, t, grid=4096):
+        assert self.lib.stream_write(t.data_ptr(), t.numel() * t.element_size(), grid,
+                                     self._st()) == 0
+
+    def copy(self, a, b, grid=4096):
+        assert self.lib.stream_copy(a.data_ptr(), b.data_ptr(), a.numel() * a.element_size(), grid,
+                                    self._st()) == 0
+
+    def flush(self):
+        """Read 512 MB (twice the memory-side cache) with ordinary, caching
+        loads: the caches end up holding clean lines of this buffer."""
+        if self.flush_buf is None:
+            self.flush_buf = self.torch.ones(512 << 20, dtype=self.torch.uint8, device=self.dev)
+        self.read(self.flush_buf, cached=True)
+
+    def ceiling(self, timed):
+        torch = self.torch
+        nbytes = 1 << 30
+        a = torch.ones(nbytes, dtype=torch.uint8, device=self.dev)
+        b = torch.empty_like(a)
+        best = {"read": (0.0, 0), "write": (0.0, 0), "copy": (0.0, 0)}
+        for grid in (1024, 2048, 4096, 8192, 16384):
+            for kind, fn, moved in (("read", lambda i: self.read(a, grid), nbytes),
+                                    ("write", lambda i: self.write(b, grid), nbytes),
+                                    ("copy", lambda i: self.copy(a, b, grid), 2 * nbytes)):
+                fn(0)
+                gbs = moved / (timed(fn, 10) * 1e-3) / 1e9
+                if gbs > best[kind][0]:
+                    best[kind] = (gbs, grid)
+        del a, b
+        return {"read_GBs": round(best["read"][0], 1), "write_GBs": round(best["write"][0], 1),
+                "copy_GBs": round(best["copy"][0], 1),
+                "grids": {k: v[1] for k, v in best.items()},
+                "how": "1 GiB buffers, plain 16-byte non-temporal loads/stores, 10 back-to-back "
+                       "launches per point, best over grids of 1024-16384 workgroups of 256 "
+                       "threads; copy counts bytes read + written"}
+
+
 def _row(us, nbytes, what):
     gbs = nbytes / (us * 1e-6) / 1e9
     return {"us": round(us, 2), "bytes": nbytes, "GBs": round(gbs, 1),
             "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_are": what}
 
 
-def other_rows(p, workloads, torch, dev, xs, timed, bound):
+def cold_warm(torch, ref, fn, nbytes, hold, calls=2, reps=20):
+    """Medians of reps single calls of fn (calls API calls), each between its
+    own event pair: cold (a read-only pass over 512 MB with caching loads
+    evicts the memory-side cache first) and warm (the call right after the
+    same call). A spin kernel queued ahead of the event pair keeps the GPU
+    busy while the host enqueues the call, so launch latency is not timed."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    fn()
+    med = {}
+    for kind in ("cold", "warm"):
+        ts = []
+        for _ in range(reps):
+            if kind == "cold":
+                ref.flush()
+            else:
+                fn()
+            hold(calls)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        med[kind] = 0.5 * (ts[(reps - 1) // 2] + ts[reps // 2])
+    out = {"bytes": nbytes, "bytes_are": "X read by the amax and the cast passes, both copies "
+                                          "written (algorithmic)"}
+    for kind, us in med.items():
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[f"{kind}_us"] = round(us, 2)
+        out[f"{kind}_GBs"] = round(gbs, 1)
+        out[f"{kind}_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+    out["how"] = (f"median of {reps} single calls each, a spin kernel queued ahead of each: "
+                  "cold after a 512 MB read-only pass with caching loads, warm right after the "
+                  "same call")
+    return out
+
+
+def other_rows(p, workloads, torch, dev, xs, timed, bound, ref, hold):
     """The remaining kernels of the path, each on the workload it serves,
     timed alone (back-to-back launches, events at the region's ends). Bytes
     are those each launch actually has to move (the two-kernel amax reads X
@@ -144,6 +266,13 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
     res["fp32_4097x2880_two_kernel_amax"] = _row(timed(fa, n) * 1e3, 2 * M * K * 4 + 4 * (M + K),
                                                  "X read by each of the two kernels")
     res["fp32_4097x2880_cast"] = _row(timed(fc, n) * 1e3, cb, "X read once, both copies written")
+    fac = lambda i: (fa(i), fc(i))
+    res["fp32_4097x2880_amax_and_cast"] = _row(
+        timed(fac, n, 2) * 1e3, workloads.algorithmic_bytes(M, K, 4),
+        "the whole quantize (two-kernel amax, then cast), back to back; algorithmic bytes "
+        "(X counted twice)")
+    res["fp32_4097x2880_amax_and_cast"].update(
+        cold_warm(torch, ref, lambda: fac(0), workloads.algorithmic_bytes(M, K, 4), hold))
     del x, out
 
     w = workloads.make("moe_groups")
@@ -181,26 +310,10 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
         timed(grouped, n) * 1e3, gb, "token rows read by the amax and the cast, padded layout written")
     del tok, out
 
-    # the two small matrices, one whole quantize each (amax pass + cast),
-    # cold: a 512 MB fill evicts the memory-side cache before every rep, and
-    # the median of the reps is reported (the 256 x 256 case is launch-bound)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-
-    def cold(fn, reps=20):
-        fn()
-        ts = []
-        for i in range(reps):
-            flush.fill_(i & 0xFF)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ts.sort()
-        return 0.5 * (ts[(reps - 1) // 2] + ts[reps // 2])
-
+    # the two small matrices, one whole quantize each (amax pass + cast):
+    # median of 20 cold repetitions (the memory-side cache evicted by a
+    # read-only pass before each) and of 20 warm ones (the same call again
+    # right after itself); the 256 x 256 case is launch-bound
     for name in ("tiny_rowscale", "outliers"):
         w = workloads.make(name)
         M, K = w.shape
@@ -220,17 +333,14 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound):
             p.nvfp4_quantize_transpose(x, 0, ta, 0, ta, bound, out["q_row"], out["s_row"],
                                        out["q_col"], out["s_col"])
 
-        res["%s_%dx%d_row_scaled_cold" % (name, M, K)] = _row(
-            cold(row_scaled) * 1e3, workloads.algorithmic_bytes(M, K, 2),
-            "X read by the amax and the cast passes, both copies written; median of 20 cold reps")
+        res["%s_%dx%d_row_scaled" % (name, M, K)] = cold_warm(
+            torch, ref, row_scaled, workloads.algorithmic_bytes(M, K, 2), hold)
         if name == "outliers":
-            res["%s_%dx%d_per_tensor_cold" % (name, M, K)] = _row(
-                cold(per_tensor) * 1e3,
+            res["%s_%dx%d_per_tensor" % (name, M, K)] = cold_warm(
+                torch, ref, per_tensor,
                 workloads.algorithmic_bytes(M, K, 2, row_amax=False, col_amax=False,
-                                            tensor_amax=True),
-                "X read by the amax and the cast passes, both copies written; median of 20 cold reps")
+                                            tensor_amax=True), hold)
         del x, out
-    del flush
     return res
 
 
@@ -358,6 +468,7 @@ def main():
     torch.cuda.synchronize()
 
     K_steps = args.steps
+    step_bytes = workloads.algorithmic_bytes(M, K, 2)
     # headline: K whole steps
     ms_per_step = timed(lambda i: (amax(i), cast(i)), K_steps, 2)
     # per-kernel regions: the same launches, one kind at a time
@@ -375,12 +486,44 @@ def main():
     cast_step = sum(a.elapsed_time(b) for a, b in ev) / K_steps
     cast_avg = timed(cast, K_steps)
     amax_avg = timed(amax, K_steps)
-    step_bytes = workloads.algorithmic_bytes(M, K, 2)
     cast_bytes = M * K * 2 + 4 * (M + K) + (M * ((K + 1) // 2) + M * ((K + 15) // 16)
                                             + K * ((M + 1) // 2) + K * ((M + 15) // 16))
     amax_bytes = M * K * 2 + 4 * (M + K)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     cast_gbs = cast_bytes / (cast_step * 1e-3) / 1e9
+
+    # The fused-amax PR's own comparison ("Performance"): the median latency
+    # of the whole quantize with the fused amax pass against the same quantize
+    # with the separate row and column amax kernels. Regions of 100 steps of
+    # each kind alternate, and the median of the region means is reported.
+    def amax2(i):
+        p.nvfp4_amax_rowcol(xs[i & 1], ra, ca, flags=p.NVFP4_FLAG_FORCE_TWO_KERNEL)
+
+    for i in range(4):
+        amax2(i)
+        cast(i)
+    fused_r, two_r = [], []
+    for _ in range(11):
+        fused_r.append(timed(lambda i: (amax(i), cast(i)), 100, 2))
+        two_r.append(timed(lambda i: (amax2(i), cast(i)), 100, 2))
+    fused_r.sort()
+    two_r.sort()
+    fused_med, two_med = fused_r[5] * 1e3, two_r[5] * 1e3
+    full_cmp = {
+        "fused_amax_then_cast_us": round(fused_med, 2),
+        "row_amax_col_amax_then_cast_us": round(two_med, 2),
+        "speedup": round(two_med / fused_med, 3),
+        "fused_GBs": round(step_bytes / (fused_med * 1e-6) / 1e9, 1),
+        "how": "median of 11 region means, each region 100 whole quantizes (amax init + "
+               "amax kernels + cast) back to back; fused and two-kernel regions alternate",
+        "pages": "fused-amax PR 'Performance': full-quantize median latency, fused amax + cast "
+                 "against row amax + column amax + cast, on one Blackwell SM100 (GB200); its "
+                 "values did not survive the text extraction, so there is no number to set "
+                 "these against",
+    }
+
+    ref = StreamRef(torch, dev)
+    ceiling = ref.ceiling(timed)
 
     # dequantize the rowwise copy to BF16 (reported beside the step, not in it)
     y = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
@@ -391,7 +534,8 @@ def main():
     dq_bytes = M * ((K + 1) // 2) + M * ((K + 15) // 16) + 4 * M + M * K * 2
     del y
 
-    row_meas = {} if args.no_rows else other_rows(p, workloads, torch, dev, xs, timed, bound)
+    row_meas = {} if args.no_rows else other_rows(p, workloads, torch, dev, xs, timed, bound, ref,
+                                                        hold_queue)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -421,7 +565,8 @@ def main():
         dt1 = time.perf_counter() - t1
         oracle.set_threads(threads)
         cpu = {"value": round(reps * workloads.algorithmic_bytes(rows, K, 2) / dt / 1e9, 4),
-               "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "unit": "GB/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+               "host_cpus_available": len(os.sched_getaffinity(0)),
                "sample": f"{reps} pass(es) over the first {rows} rows x {K} columns of the same "
                          f"matrix (as its own {rows}x{K} input): amax rows+cols, then both "
                          f"quantize directions; {dt:.1f} s wall",
@@ -457,12 +602,16 @@ def main():
                        "cast_back_to_back": round(cast_avg * 1e3, 2),
                        "amax_GBs": round(amax_bytes / (amax_avg * 1e-3) / 1e9, 1),
                        "how": "each kind launched alone, back to back, same inputs"},
+        "full_quantize_fused_vs_two_kernel": full_cmp,
+        "hbm_measured": dict(ceiling, step_frac_of_copy=round(value / ceiling["copy_GBs"], 4),
+                             cast_frac_of_copy=round(cast_gbs / ceiling["copy_GBs"], 4)),
         "dequant_rowwise_bf16": {"us": round(dq_ms * 1e3, 2),
                                  "GBs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1),
                                  "frac": round(dq_bytes / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "other_rows": row_meas,
         "cpu_baseline": cpu,
         "source_digest": source_digest(),
+        "library": os.path.relpath(p.library_path(), ROOT),
     }
     print(json.dumps(rec))
 

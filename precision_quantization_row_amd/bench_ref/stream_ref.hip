@@ -1,0 +1,111 @@
+// stream_ref.hip -- reference streaming kernels for measuring what this GPU's
+// HBM sustains (the achievable ceiling printed next to the quantize path's
+// bandwidth). Not part of the NVFP4 library: plain 16-byte non-temporal reads,
+// writes and copies over a buffer, grid-stride, with nothing else per byte.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+// Reads every 16-byte vector once and folds it into a register; the fold is
+// stored only if it equals a value the caller can never arrange for all
+// lanes (`never`), so no load can be removed. NT: non-temporal loads (the
+// ceiling); otherwise ordinary loads, which allocate in the caches (the
+// read-only cache flush).
+template <bool NT>
+__global__ void __launch_bounds__(kThreads) read_kernel(const u32x4* __restrict__ x, int64_t n,
+                                                        uint32_t never, uint32_t* sink) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t acc = 0u;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = load16<NT>(x + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n; i += stride) {
+    const u32x4 v = load16<NT>(x + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == never) sink[0] = acc;
+}
+
+__global__ void __launch_bounds__(kThreads) write_kernel(u32x4* __restrict__ y, int64_t n,
+                                                         uint32_t v) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const u32x4 w = {v, v, v, v};
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
+    __builtin_nontemporal_store(w, y + i);
+}
+
+__global__ void __launch_bounds__(kThreads) copy_kernel(const u32x4* __restrict__ x,
+                                                        u32x4* __restrict__ y, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(x + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(v[u], y + i + u * stride);
+  }
+  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(x + i), y + i);
+}
+
+bool ok(const void* p, int64_t bytes) {
+  return p != nullptr && bytes > 0 && bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+}
+
+int done() { return hipGetLastError() == hipSuccess ? 0 : -3; }
+
+}  // namespace
+
+extern "C" {
+
+// Each returns -1 for a bad argument (NULL, size not a positive multiple of
+// 16, pointer not 16-byte aligned, grid < 1), else 0 or -3 after enqueuing
+// one kernel of `grid` workgroups of 256 threads on `stream`.
+// cached != 0: ordinary loads (they allocate in the caches) instead of
+// non-temporal ones.
+int stream_read(const void* x, int64_t bytes, uint32_t* sink, int grid, int cached, void* stream) {
+  if (!ok(x, bytes) || sink == nullptr || grid < 1) return -1;
+  if (cached)
+    hipLaunchKernelGGL(read_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(x), bytes / 16,
+                       0xC0FFEE11u, sink);
+  else
+    hipLaunchKernelGGL(read_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(x), bytes / 16,
+                       0xC0FFEE11u, sink);
+  return done();
+}
+
+int stream_write(void* y, int64_t bytes, int grid, void* stream) {
+  if (!ok(y, bytes) || grid < 1) return -1;
+  hipLaunchKernelGGL(write_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<u32x4*>(y), bytes / 16, 0u);
+  return done();
+}
+
+int stream_copy(const void* x, void* y, int64_t bytes, int grid, void* stream) {
+  if (!ok(x, bytes) || !ok(y, bytes) || grid < 1) return -1;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(x),
+                     static_cast<u32x4*>(y), bytes / 16);
+  return done();
+}
+
+}  // extern "C"
