@@ -136,7 +136,7 @@ class StreamRef:
         a = torch.ones(nbytes, dtype=torch.uint8, device=self.dev)
         b = torch.empty_like(a)
         best = {"read": (0.0, 0), "write": (0.0, 0), "copy": (0.0, 0)}
-        for grid in (1024, 2048, 4096, 8192, 16384):
+        for grid in (512, 1024, 2048, 4096, 8192, 16384):
             for kind, fn, moved in (("read", lambda i: self.read(a, grid), nbytes),
                                     ("write", lambda i: self.write(b, grid), nbytes),
                                     ("copy", lambda i: self.copy(a, b, grid), 2 * nbytes)):
@@ -148,9 +148,10 @@ class StreamRef:
         return {"read_GBs": round(best["read"][0], 1), "write_GBs": round(best["write"][0], 1),
                 "copy_GBs": round(best["copy"][0], 1),
                 "grids": {k: v[1] for k, v in best.items()},
-                "how": "1 GiB buffers, plain 16-byte non-temporal loads/stores, 10 back-to-back "
-                       "launches per point, best over grids of 1024-16384 workgroups of 256 "
-                       "threads; copy counts bytes read + written"}
+                "how": "1 GiB buffers, plain 16-byte non-temporal loads/stores (4 in flight per "
+                       "thread, 1 KB contiguous per wave instruction), 10 back-to-back launches "
+                       "per point, best over grids of 512-16384 workgroups of 256 threads; copy "
+                       "counts bytes read + written"}
 
 
 def _row(us, nbytes, what):

@@ -18,6 +18,11 @@ __device__ __forceinline__ u32x4 load16(const u32x4* p) {
   else return *p;
 }
 
+// Every kernel walks the buffer in chunks of kUnroll * 256 vectors (16 KB):
+// workgroup b takes chunks b, b + grid, b + 2 grid, ...; in a chunk, load u
+// of thread t is vector u * 256 + t, so each instruction of a wave covers
+// 1 KB of contiguous memory and a thread keeps kUnroll loads in flight.
+
 // Reads every 16-byte vector once and folds it into a register; the fold is
 // stored only if it equals a value the caller can never arrange for all
 // lanes (`never`), so no load can be removed. NT: non-temporal loads (the
@@ -26,43 +31,53 @@ __device__ __forceinline__ u32x4 load16(const u32x4* p) {
 template <bool NT>
 __global__ void __launch_bounds__(kThreads) read_kernel(const u32x4* __restrict__ x, int64_t n,
                                                         uint32_t never, uint32_t* sink) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
   uint32_t acc = 0u;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+  for (int64_t c = blockIdx.x; c * kChunk < n; c += gridDim.x) {
+    const int64_t b = c * kChunk + threadIdx.x;
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = load16<NT>(x + i + u * stride);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = b + u * kThreads;
+      v[u] = i < n ? load16<NT>(x + i) : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-  }
-  for (; i < n; i += stride) {
-    const u32x4 v = load16<NT>(x + i);
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == never) sink[0] = acc;
 }
 
 __global__ void __launch_bounds__(kThreads) write_kernel(u32x4* __restrict__ y, int64_t n,
                                                          uint32_t v) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
   const u32x4 w = {v, v, v, v};
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
-    __builtin_nontemporal_store(w, y + i);
+  for (int64_t c = blockIdx.x; c * kChunk < n; c += gridDim.x) {
+    const int64_t b = c * kChunk + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = b + u * kThreads;
+      if (i < n) __builtin_nontemporal_store(w, y + i);
+    }
+  }
 }
 
 __global__ void __launch_bounds__(kThreads) copy_kernel(const u32x4* __restrict__ x,
                                                         u32x4* __restrict__ y, int64_t n) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (kUnroll - 1) * stride < n; i += kUnroll * stride) {
+  constexpr int64_t kChunk = (int64_t)kThreads * kUnroll;
+  for (int64_t c = blockIdx.x; c * kChunk < n; c += gridDim.x) {
+    const int64_t b = c * kChunk + threadIdx.x;
     u32x4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(x + i + u * stride);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = b + u * kThreads;
+      if (i < n) v[u] = __builtin_nontemporal_load(x + i);
+    }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) __builtin_nontemporal_store(v[u], y + i + u * stride);
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = b + u * kThreads;
+      if (i < n) __builtin_nontemporal_store(v[u], y + i);
+    }
   }
-  for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(x + i), y + i);
 }
 
 bool ok(const void* p, int64_t bytes) {
