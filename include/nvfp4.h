@@ -81,12 +81,14 @@ enum { NVFP4_FLAG_FORCE_TWO_KERNEL = 1u }; /* skip the fused amax kernel */
 /* Which amax kernels nvfp4_amax_rowcol runs for these arguments.
  * Returns 1 for the fused row+column pass, 2 for the separate row / column
  * kernels, 0 when neither vector is requested. Host-only; enqueues nothing.
- * The fused pass runs only for BF16 input with M % 128 == 0, K % 128 == 0,
- * both row and column vectors requested, the flag clear and the environment
- * variable NVFP4_FUSED_AMAX not set to "0" (the gate and kill switch of the
- * fused-amax PR description). nvfp4_amax_rowcol also sends an X that is not
- * 16-byte aligned to the separate kernels. Both paths give identical bits
- * (exact max). */
+ * The fused pass runs when both row and column vectors are requested, X's
+ * rows are whole 16-byte vectors (K % 8 == 0 for BF16, K % 4 == 0 for
+ * FP32), the flag is clear and the environment variable NVFP4_FUSED_AMAX is
+ * not "0" (the kill switch of the fused-amax PR description; its gate, BF16
+ * with 128-aligned dimensions, is what its TMA tiles need, and this pass
+ * has no such need). nvfp4_amax_rowcol also sends an X that is not 16-byte
+ * aligned to the separate kernels. Both paths give identical bits (exact
+ * max). */
 int nvfp4_amax_path(int in_dtype, int64_t M, int64_t K, int want_row, int want_col,
                     unsigned flags);
 

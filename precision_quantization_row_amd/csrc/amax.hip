@@ -37,29 +37,58 @@ __global__ void __launch_bounds__(256) amax_init_kernel(float* ra, int64_t M, fl
   if (ta && t0 == 0) ta[0] = 0.0f;
 }
 
-// ------------------------------------------------------------- fused (BF16)
-// Workgroup = 4 waves; a wave's 16-lane DPP row g reads 16 x 16 B = 128
-// consecutive BF16 of one row per load, so every load instruction fetches 4
-// full 256-byte row segments. The tile is tr rows x (128 * FUSED_NC) columns
-// (tr = 256, or fewer for small matrices so that the grid still fills the
-// GPU); the 16 (wave, row-group) slots take rows slot, slot + 16, ...
-// Each lane keeps the running column max of its 8 * FUSED_NC columns in
-// registers as packed u16 magnitudes (v_pk_max_u16), so the column reduction
-// is a register reduction over rows -- no strided global read and no LDS
-// staging of the tile. Row maxima are reduced across the 16 lanes with DPP;
-// column maxima of the 16 slots meet once in LDS; both are published with
-// atomic max at the end of the tile, one per row and one per column.
-constexpr int FUSED_NC = 4;    // 128-column chunks per tile -> 512 columns
+// ------------------------------------------------------------------ fused
+// Workgroup = 4 waves; a wave's 16-lane DPP row g reads 16 x 16 B of one row
+// per load (128 BF16 or 64 FP32 columns: a "chunk"), so every load
+// instruction fetches 4 full 256-byte row segments. The tile is tr rows x
+// FUSED_NC chunks (tr = 256, or fewer for small matrices so that the grid
+// still fills the GPU); the 16 (wave, row-group) slots take rows slot,
+// slot + 16, ... Each lane keeps the running column max of its columns in
+// registers (BF16: packed u16 magnitudes, v_pk_max_u16; FP32: one magnitude
+// per dword), so the column reduction is a register reduction over rows --
+// no strided global read and no LDS staging of the tile. Row maxima are
+// reduced across the 16 lanes with DPP; column maxima of the 16 slots meet
+// once in LDS; both are published with atomic max at the end of the tile,
+// one per row and one per column.
+//
+// Any M, and any K whose rows are whole 16-byte vectors (K % 8 == 0 for
+// BF16, K % 4 == 0 for FP32) with a 16-byte aligned X: a lane's 16-byte
+// vector lies wholly inside the row or wholly past its end (then it reads
+// nothing and counts as zeros), and rows past M are skipped.
+constexpr int FUSED_NC = 4;    // chunks per tile -> 512 BF16 / 256 FP32 columns
 constexpr int FUSED_TR = 256;  // rows per tile (largest)
 constexpr int FUSED_RU = 2;    // rows per slot per loop iteration
 
-__global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __restrict__ x,
-                                                              int64_t M, int64_t K,
-                                                              float* __restrict__ ra,
-                                                              float* __restrict__ ca,
-                                                              const float* noop,
-                                                              int64_t tiles_c, int64_t tr) {
+template <typename T>
+struct FusedGeom {
+  static constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
+  static constexpr int CH = 16 * V;         // columns per chunk
+  static constexpr int TC = CH * FUSED_NC;  // columns per tile
+};
+
+// Magnitude bits of one dword's elements, maxed into acc (BF16: two packed
+// u16 magnitudes; FP32: one).
+template <typename T>
+__device__ __forceinline__ uint32_t mag_max(uint32_t acc, uint32_t w) {
+  if constexpr (sizeof(T) == 2) return pk_max_u16(acc, w & kAbsBf16x2);
+  else return max(acc, w & kAbsF32);
+}
+
+// The FP32 bit pattern of the largest magnitude held in acc.
+template <typename T>
+__device__ __forceinline__ uint32_t mag_bits(uint32_t acc) {
+  if constexpr (sizeof(T) == 2) return max(acc & 0xFFFFu, acc >> 16) << 16;
+  else return acc;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) fused_amax_kernel(const T* __restrict__ x, int64_t M,
+                                                         int64_t K, float* __restrict__ ra,
+                                                         float* __restrict__ ca,
+                                                         const float* noop, int64_t tiles_c,
+                                                         int64_t tr) {
   if (skip(noop)) return;
+  using G = FusedGeom<T>;
   __shared__ uint32_t colmax_s[16][FUSED_NC * 64 + 1];
   __shared__ uint32_t rowmax_s[FUSED_TR];  // the tile's row maxima, published at the end
   const int tid = threadIdx.x;
@@ -68,7 +97,7 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
   const int slot = (tid >> 6) * 4 + (lane >> 4);  // 0..15
   const int64_t tile = blockIdx.x;
   const int64_t r0 = (tile / tiles_c) * tr;
-  const int64_t c0 = (tile % tiles_c) * (128 * FUSED_NC);
+  const int64_t c0 = (tile % tiles_c) * G::TC;
 
   uint32_t cm[FUSED_NC][4];
 #pragma unroll
@@ -76,21 +105,22 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
 #pragma unroll
     for (int d = 0; d < 4; ++d) cm[j][d] = 0u;
 
+  // the lane's vector of chunk j: inside the row or wholly past its end
   bool colok[FUSED_NC];
 #pragma unroll
-  for (int j = 0; j < FUSED_NC; ++j) colok[j] = (c0 + 128 * j) < K;  // K % 128 == 0
+  for (int j = 0; j < FUSED_NC; ++j) colok[j] = (c0 + G::CH * j + G::V * q) < K;
 
   const int64_t rend = min(r0 + tr, M);
   // FUSED_RU rows per slot and iteration, all loads issued before any use
-  // (rows past rend are skipped; with M % 128 == 0 and tr a multiple of 32
-  // that only happens for RU = 4 and 32-row tiles)
+  // (rows past rend are skipped).
   //
   // The first half of the tile's rows is read with non-temporal loads, the
   // second half with ordinary ones: X is read again by the cast right after
   // this pass, and what this pass reads last is what the caches still hold
-  // then. Measured on 8192 x 28672 (same GPU, step = this pass + the cast):
-  // streamed fraction 0: 217 us, 1/4: 209, 3/8: 207, 1/2: 205-207, 5/8: 207,
-  // 3/4: 208-209 (this pass alone: 87 us with none streamed, 79.6 with half).
+  // then. Measured on 8192 x 28672 BF16 (same GPU, step = this pass + the
+  // cast): streamed fraction 0: 217 us, 1/4: 209, 3/8: 207, 1/2: 205-207,
+  // 5/8: 207, 3/4: 208-209 (this pass alone: 87 us with none streamed, 79.6
+  // with half).
   const int64_t r_stream = r0 + tr / 2;
   for (int64_t rb = r0 + slot; rb < rend; rb += 16 * FUSED_RU) {
     uint4 v[FUSED_RU][FUSED_NC];
@@ -119,16 +149,14 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
       uint32_t rm = 0u;
 #pragma unroll
       for (int j = 0; j < FUSED_NC; ++j) {
-        const uint32_t a0 = v[u][j].x & kAbsBf16x2, a1 = v[u][j].y & kAbsBf16x2;
-        const uint32_t a2 = v[u][j].z & kAbsBf16x2, a3 = v[u][j].w & kAbsBf16x2;
-        cm[j][0] = pk_max_u16(cm[j][0], a0);
-        cm[j][1] = pk_max_u16(cm[j][1], a1);
-        cm[j][2] = pk_max_u16(cm[j][2], a2);
-        cm[j][3] = pk_max_u16(cm[j][3], a3);
-        rm = pk_max_u16(rm, pk_max_u16(pk_max_u16(a0, a1), pk_max_u16(a2, a3)));
+        cm[j][0] = mag_max<T>(cm[j][0], v[u][j].x);
+        cm[j][1] = mag_max<T>(cm[j][1], v[u][j].y);
+        cm[j][2] = mag_max<T>(cm[j][2], v[u][j].z);
+        cm[j][3] = mag_max<T>(cm[j][3], v[u][j].w);
+        rm = mag_max<T>(mag_max<T>(mag_max<T>(mag_max<T>(rm, v[u][j].x), v[u][j].y), v[u][j].z),
+                        v[u][j].w);
       }
-      uint32_t rbits = max(rm & 0xFFFFu, rm >> 16) << 16;
-      rbits = row16_max(rbits);
+      uint32_t rbits = row16_max(mag_bits<T>(rm));
       if (q == 0 && r < rend) rowmax_s[r - r0] = rbits;  // row r has one writer in the tile
     }
   }
@@ -143,16 +171,21 @@ __global__ void __launch_bounds__(256) fused_amax_bf16_kernel(const uint16_t* __
   // memory atomic there sits in the same in-order counter as the loads and
   // holds up the waits for the next rows.
   if (tid < rend - r0) atomicMax(reinterpret_cast<unsigned int*>(ra + r0 + tid), rowmax_s[tid]);
-  // 256 threads, FUSED_NC * 64 dwords = 2 * FUSED_NC * 64 columns
+  // 256 threads, FUSED_NC * 64 dwords (BF16: two columns each, FP32: one)
   for (int e = tid; e < FUSED_NC * 64; e += 256) {
     uint32_t m = 0u;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) m = pk_max_u16(m, colmax_s[s][e]);
-    const int j = e / 64, w = e % 64;
-    const int64_t col = c0 + 128 * j + 2 * w;  // w = q * 4 + d -> columns 8q + 2d, +1
-    if (col < K) {
-      atomicMax(reinterpret_cast<unsigned int*>(ca + col), (m & 0xFFFFu) << 16);
-      atomicMax(reinterpret_cast<unsigned int*>(ca + col + 1), m & 0xFFFF0000u);
+    for (int s = 0; s < 16; ++s) m = mag_max<T>(m, colmax_s[s][e]);  // magnitudes already
+    const int j = e / 64, w = e % 64;  // w = q * 4 + d
+    if constexpr (sizeof(T) == 2) {
+      const int64_t col = c0 + G::CH * j + 2 * w;  // columns 8q + 2d, +1
+      if (col < K) {
+        atomicMax(reinterpret_cast<unsigned int*>(ca + col), (m & 0xFFFFu) << 16);
+        atomicMax(reinterpret_cast<unsigned int*>(ca + col + 1), m & 0xFFFF0000u);
+      }
+    } else {
+      const int64_t col = c0 + G::CH * j + w;  // column 4q + d
+      if (col < K) atomicMax(reinterpret_cast<unsigned int*>(ca + col), m);
     }
   }
 }
@@ -491,18 +524,25 @@ int launch_amax_init(float* ra, int64_t M, float* ca, int64_t K, float* ta, cons
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-int launch_fused_amax_bf16(const void* x, int64_t M, int64_t K, float* ra, float* ca,
-                           const float* noop, hipStream_t s) {
-  const int64_t tiles_c = (K + 128 * FUSED_NC - 1) / (128 * FUSED_NC);
+template <typename T>
+static int launch_fused_t(const void* x, int64_t M, int64_t K, float* ra, float* ca,
+                          const float* noop, hipStream_t s) {
+  const int64_t tiles_c = (K + FusedGeom<T>::TC - 1) / FusedGeom<T>::TC;
   // Tall tiles publish fewer column maxima; short ones give more workgroups.
   // Take the tallest tile (256 .. 32 rows) that still gives about 6
   // workgroups per CU.
   int64_t tr = FUSED_TR;
   while (tr > 32 && ((M + tr - 1) / tr) * tiles_c < (int64_t)num_cus() * 6) tr /= 2;
   const int64_t tiles_r = (M + tr - 1) / tr;
-  hipLaunchKernelGGL(fused_amax_bf16_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), M, K, ra, ca, noop, tiles_c, tr);
+  hipLaunchKernelGGL(fused_amax_kernel<T>, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, s,
+                     static_cast<const T*>(x), M, K, ra, ca, noop, tiles_c, tr);
   return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int launch_fused_amax(const void* x, int in_dtype, int64_t M, int64_t K, float* ra, float* ca,
+                      const float* noop, hipStream_t s) {
+  return in_dtype == 0 ? launch_fused_t<uint16_t>(x, M, K, ra, ca, noop, s)
+                       : launch_fused_t<float>(x, M, K, ra, ca, noop, s);
 }
 
 template <typename T>

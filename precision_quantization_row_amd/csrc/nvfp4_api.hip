@@ -55,8 +55,10 @@ const char* nvfp4_status_string(int status) {
 
 int nvfp4_amax_path(int in_dtype, int64_t M, int64_t K, int want_row, int want_col, unsigned flags) {
   if (!want_row && !want_col) return 0;
-  const bool fused = want_row && want_col && in_dtype == NVFP4_BF16 && M > 0 && K > 0 &&
-                     M % 128 == 0 && K % 128 == 0 && !(flags & NVFP4_FLAG_FORCE_TWO_KERNEL) &&
+  // rows of whole 16-byte vectors: K % 8 == 0 (BF16), K % 4 == 0 (FP32)
+  const int64_t v = in_dtype == NVFP4_BF16 ? 8 : 4;
+  const bool fused = want_row && want_col && (in_dtype == NVFP4_BF16 || in_dtype == NVFP4_FP32) &&
+                     M > 0 && K > 0 && K % v == 0 && !(flags & NVFP4_FLAG_FORCE_TWO_KERNEL) &&
                      fused_env_enabled();
   return fused ? 1 : 2;
 }
@@ -78,7 +80,7 @@ int nvfp4_amax_rowcol(const void* x, int in_dtype, int64_t M, int64_t K, float* 
   // alignment itself
   if (path == 1 && (reinterpret_cast<uintptr_t>(x) & 15) != 0) path = 2;
   if (path == 1)
-    rc = launch_fused_amax_bf16(x, M, K, row_amax, col_amax, noop, s);
+    rc = launch_fused_amax(x, in_dtype, M, K, row_amax, col_amax, noop, s);
   else if (path == 2)
     rc = launch_row_col_amax(x, in_dtype, M, K, row_amax, col_amax, noop, s);
   if (rc) return NVFP4_ERR_HIP;

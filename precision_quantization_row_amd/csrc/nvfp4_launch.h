@@ -13,8 +13,8 @@ int num_cus();
 
 int launch_amax_init(float* ra, int64_t M, float* ca, int64_t K, float* ta, const float* noop,
                      hipStream_t s);
-int launch_fused_amax_bf16(const void* x, int64_t M, int64_t K, float* ra, float* ca,
-                           const float* noop, hipStream_t s);
+int launch_fused_amax(const void* x, int in_dtype, int64_t M, int64_t K, float* ra, float* ca,
+                      const float* noop, hipStream_t s);
 int launch_row_col_amax(const void* x, int in_dtype, int64_t M, int64_t K, float* ra, float* ca,
                         const float* noop, hipStream_t s);
 int launch_tensor_amax(const void* x, int in_dtype, int64_t n, float* ta, const float* noop,

@@ -40,9 +40,11 @@ def test_status_strings():
 @pytest.mark.parametrize("dtype,M,K,row,col,flags,want", [
     (p.NVFP4_BF16, 256, 512, 1, 1, 0, 1),
     (p.NVFP4_BF16, 8192, 28672, 1, 1, 0, 1),
-    (p.NVFP4_FP32, 256, 512, 1, 1, 0, 2),      # FP32 -> two kernels
-    (p.NVFP4_BF16, 257, 512, 1, 1, 0, 2),      # unaligned M
-    (p.NVFP4_BF16, 256, 520, 1, 1, 0, 2),      # unaligned K
+    (p.NVFP4_FP32, 256, 512, 1, 1, 0, 1),      # FP32 too
+    (p.NVFP4_FP32, 4097, 2880, 1, 1, 0, 1),    # ragged M and K with 16-byte rows
+    (p.NVFP4_BF16, 257, 520, 1, 1, 0, 1),
+    (p.NVFP4_BF16, 256, 524, 1, 1, 0, 2),      # rows that are not whole 16-byte vectors
+    (p.NVFP4_FP32, 256, 514, 1, 1, 0, 2),
     (p.NVFP4_BF16, 256, 512, 1, 0, 0, 2),      # one direction only
     (p.NVFP4_BF16, 256, 512, 0, 1, 0, 2),
     (p.NVFP4_BF16, 256, 512, 1, 1, p.NVFP4_FLAG_FORCE_TWO_KERNEL, 2),

@@ -72,6 +72,36 @@ def test_fused_amax_tile_heights(M, K):
     assert_same("col_amax", f32_bits(ca), oracle.amax_cols(xf).view(np.uint32))
 
 
+@pytest.mark.parametrize("dtype,M,K", [
+    (torch.float32, 4097, 2880), (torch.float32, 1, 4), (torch.float32, 17, 260),
+    (torch.float32, 300, 1028), (torch.float32, 33, 65540 // 4 * 4), (torch.float32, 1000, 12),
+    (torch.bfloat16, 1, 8), (torch.bfloat16, 257, 520), (torch.bfloat16, 129, 4104),
+    (torch.bfloat16, 4097, 2888), (torch.bfloat16, 70, 24)])
+def test_fused_amax_ragged_and_fp32(dtype, M, K):
+    """The one-pass amax on shapes outside the 128-aligned BF16 case: FP32,
+    ragged M, and K that ends inside a chunk or a tile (only whole 16-byte
+    row vectors are required). Values over the whole exponent range of the
+    type (FP32 subnormals and magnitudes up to FLT_MAX / 448 included); exact
+    maxima, identical to the two-kernel path."""
+    say(f"[gpu] fused amax {M}x{K} {dtype}")
+    g = torch.Generator().manual_seed(M * 7 + K)
+    e = torch.randint(-140, 120, (M, 1), generator=g).float() if dtype == torch.float32 else \
+        torch.randint(-130, 120, (M, 1), generator=g).float()
+    x = (torch.randn(M, K, generator=g) * torch.pow(2.0, e)).to(dtype)
+    x[torch.rand(M, K, generator=g) < 0.01] = 0.0
+    assert torch.isfinite(x.float()).all()
+    assert p.nvfp4_amax_path(p.NVFP4_BF16 if dtype == torch.bfloat16 else p.NVFP4_FP32,
+                             M, K, 1, 1, 0) == 1
+    xd = x.to(DEV)
+    ra, ca, _ = gpu_amax(xd)
+    xf = x.float().numpy()
+    assert_same("row_amax", f32_bits(ra), oracle.amax_rows(xf).view(np.uint32))
+    assert_same("col_amax", f32_bits(ca), oracle.amax_cols(xf).view(np.uint32))
+    ra2, ca2, _ = gpu_amax(xd, flags=p.NVFP4_FLAG_FORCE_TWO_KERNEL)
+    assert_same("row two-kernel", f32_bits(ra2), f32_bits(ra))
+    assert_same("col two-kernel", f32_bits(ca2), f32_bits(ca))
+
+
 @pytest.mark.parametrize("M,K", [(128, 256), (384, 768), (640, 256), (192, 512), (448, 512)])
 def test_interior_half_macro_tiles(M, K):
     """M % 256 = 128 or 192: the interior kernel's last macro row is a 128-row

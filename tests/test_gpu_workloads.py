@@ -131,11 +131,15 @@ def test_moe_groups_full():
                 oracle_dequant_bits(qc, sc, K, M, oracle.MODE_ROWGROUP, ex_o, 448.0, torch.bfloat16))
 
 
-def test_fp32_edge_full():
+@pytest.mark.parametrize("flags", [0, p.NVFP4_FLAG_FORCE_TWO_KERNEL])
+def test_fp32_edge_full(flags):
+    """FP32 4097 x 2880 with its planted structure, both bounds, through the
+    one-pass amax (the default for 16-byte rows) and through the two-kernel
+    amax path."""
     w = workloads.make("fp32_edge")
     M, K = w.shape
-    assert p.nvfp4_amax_path(p.NVFP4_FP32, M, K, 1, 1, 0) == 2
-    x, ra, ca = check_row_scaled(w.x, bounds=(448.0, 256.0), label="fp32_edge")
+    assert p.nvfp4_amax_path(p.NVFP4_FP32, M, K, 1, 1, flags) == (2 if flags else 1)
+    x, ra, ca = check_row_scaled(w.x, bounds=(448.0, 256.0), flags=flags, label="fp32_edge")
     zr = w.notes["zero_row"]
     out = gpu_quantize(x, 1, ra, 1, ca, 448.0)
     assert not out["q_row"][zr].any() and not out["s_row"][zr].any()
