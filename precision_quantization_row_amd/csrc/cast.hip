@@ -976,10 +976,88 @@ __device__ __forceinline__ WaveRows grouped_wave_rows(const SM& sm, int G, uint3
   return w;
 }
 
+// The whole aligned dwords of bytes [lo, hi) of a 128-byte column segment,
+// to the global address A of any alignment. This lane (t of the column's 8
+// consecutive lanes) holds the segment's dwords S[4t .. 4t + 3] and prev =
+// S[4t - 1] (from lane t - 1). Output dword m lies at E + 4m, E = A - A % 4,
+// and holds segment bytes 4m - A % 4 .. +3, built from S[m - 1] and S[m] with
+// a byte funnel shift; lane 7 also builds the dword past S[31]. Only dwords
+// whose four bytes all lie in [lo, hi) are written here (an aligned, whole
+// 16-byte piece as one non-temporal store, as in the aligned flush);
+// store_segment_ends writes the at most 3 + 3 bytes at the two ends.
+__device__ __forceinline__ void store_segment_dwords(uint8_t* A, const u32x4& q, uint32_t prev,
+                                                     int t, int lo, int hi) {
+  const uint32_t ra = (uint32_t)(reinterpret_cast<uintptr_t>(A) & 3);
+  if (16 * t + 16 - (int)ra + (t == 7 ? 4 : 0) <= lo || 16 * t - (int)ra >= hi) return;
+  if ((reinterpret_cast<uintptr_t>(A + 16 * t) & 15) == 0 && 16 * t >= lo && 16 * t + 16 <= hi) {
+    __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(A + 16 * t));
+    return;
+  }
+  uint8_t* E = A - ra;
+  const uint32_t sv[5] = {prev, q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    if (i == 4 && t != 7) break;
+    const int m = 4 * t + i;
+    const int b0 = 4 * m - (int)ra;
+    if (b0 >= lo && b0 + 4 <= hi) {
+      const uint32_t cur = i < 4 ? sv[i + 1] : 0u;
+      const uint32_t val = ra ? __builtin_amdgcn_alignbyte(cur, sv[i], 4u - ra) : cur;
+      *reinterpret_cast<uint32_t*>(E + 4 * m) = val;
+    }
+  }
+}
+
+// The bytes of [lo, hi) that store_segment_dwords leaves: those before the
+// first aligned address and from the last aligned address on (all of them
+// when no whole aligned dword fits). seg(b) reads segment byte b.
+template <class Seg>
+__device__ __forceinline__ void store_segment_ends(uint8_t* A, int lo, int hi, const Seg& seg) {
+  const int f = lo + (int)((4u - (uint32_t)(reinterpret_cast<uintptr_t>(A + lo) & 3)) & 3u);
+  const int l = hi - (int)(reinterpret_cast<uintptr_t>(A + hi) & 3);
+  if (f >= l) {
+    for (int b = lo; b < hi; ++b) A[b] = seg(b);
+  } else {
+    for (int b = lo; b < f; ++b) A[b] = seg(b);
+    for (int b = l; b < hi; ++b) A[b] = seg(b);
+  }
+}
+
+// Bytes [lo, hi) (0 <= lo < hi <= 16) of 16 bytes in LDS to the global
+// address dst + lo .. of any alignment: one 16-byte store when aligned and
+// whole, four dwords when dword-aligned and whole, else byte by byte (on
+// this GPU the plain byte stores ran faster than dwords built with funnel
+// shifts, whose partial end dwords diverge).
+__device__ __forceinline__ void store_bytes_any(uint8_t* dst, const uint8_t* src, int lo, int hi) {
+  if (((reinterpret_cast<uintptr_t>(dst) & 15) == 0) && lo == 0 && hi == 16) {
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    return;
+  }
+  if (((reinterpret_cast<uintptr_t>(dst) & 3) == 0) && lo == 0 && hi == 16) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+    uint32_t* d = reinterpret_cast<uint32_t*>(dst);
+    d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    return;
+  }
+  for (int b = lo; b < hi; ++b) dst[b] = src[b];
+}
+
 // VAR: 0 = 1x16 blocks, 1 = grouped tokens (1x16), 2 = 2-D 16 x 16 blocks,
-// 3 = four-over-six 1x16 blocks (one direction per launch)
-template <typename T, bool ROWW, bool COLW, int VAR, bool SPLIT = false>
+// 3 = four-over-six 1x16 blocks (one direction per launch).
+// GEN (1x16 blocks only): any M and any K % 16 == 0 with 16-byte rows, in
+// one launch. The last strip and the last macro row may be partial: a lane
+// whose columns lie past K loads nothing (an offset past its buffer's range
+// reads as zeros) and stores nothing, rows past M read as zeros and are not
+// stored, the zero elements of a cut block change neither its maximum nor
+// its codes, and only the output bytes of existing rows and columns are
+// written. Output rows may have any alignment (odd M gives transposed rows of
+// an odd number of bytes): the transposed flush builds aligned dwords with
+// byte funnel shifts. Macro tiles are spread evenly over the XCDs (a
+// contiguous run of the strip-major tile list each), so a matrix with few
+// strips still uses every XCD.
+template <typename T, bool ROWW, bool COLW, int VAR, bool SPLIT = false, bool GEN = false>
 __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_kernel(const CastK p) {
+  static_assert(!GEN || VAR == 0, "general shapes take the 1x16 block code");
   if (p.noop != nullptr && *p.noop == 1.0f) return;
   constexpr bool GRP = VAR == 1, B2D = VAR == 2;
   constexpr int NW = Blk<T>::NW;
@@ -998,7 +1076,10 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
   const int64_t xcd = blockIdx.x % IT_XCDS, jw = blockIdx.x / IT_XCDS;
   const int64_t nstrips = p.n_istrips, nmr = p.n_isteps;  // strips, macro rows
   const int64_t spx = (nstrips + IT_XCDS - 1) / IT_XCDS;  // strips per XCD
-  const int64_t ntiles_x = nmr * spx;                     // macro tiles per XCD
+  // GEN: this XCD's run [t_lo, t_lo + ntiles_x) of the strip-major tile list
+  const int64_t t_all = nstrips * nmr;
+  const int64_t t_lo = GEN ? xcd * t_all / IT_XCDS : 0;
+  const int64_t ntiles_x = GEN ? (xcd + 1) * t_all / IT_XCDS - t_lo : nmr * spx;  // macro tiles per XCD
   const int64_t n_v = 2 * ((ntiles_x + per - 1) / per);  // sub-steps scheduled
 
   const uint32_t rowbytes = (uint32_t)(K * (int64_t)sizeof(T));
@@ -1039,13 +1120,24 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
       sub = (int)(v & 1);
       solo = false;
     }
-    // strip groups of sg strips (the XCD's last group may hold fewer), each
-    // walked macro row by macro row with its strips side by side
-    const uint32_t sg = (uint32_t)p.sgroup, gsz = sg * (uint32_t)nmr;
-    const uint32_t g = t / gsz, rem = t - g * gsz;
-    const uint32_t sgl = min(sg, (uint32_t)spx - min(g * sg, (uint32_t)spx));
-    const uint32_t r = sgl ? rem / sgl : (uint32_t)nmr, qs = rem - r * sgl;
-    const int64_t strip = xcd * spx + g * sg + qs;
+    uint32_t r;
+    int64_t strip;
+    if constexpr (GEN) {
+      // the XCD's run of the strip-major list: strip by strip, macro row by
+      // macro row
+      const uint32_t gi = (uint32_t)t_lo + t;
+      strip = gi / (uint32_t)nmr;
+      r = gi - (uint32_t)strip * (uint32_t)nmr;
+    } else {
+      // strip groups of sg strips (the XCD's last group may hold fewer), each
+      // walked macro row by macro row with its strips side by side
+      const uint32_t sg = (uint32_t)p.sgroup, gsz = sg * (uint32_t)nmr;
+      const uint32_t g = t / gsz, rem = t - g * gsz;
+      const uint32_t sgl = min(sg, (uint32_t)spx - min(g * sg, (uint32_t)spx));
+      r = sgl ? rem / sgl : (uint32_t)nmr;
+      const uint32_t qs = rem - r * sgl;
+      strip = xcd * spx + g * sg + qs;
+    }
     m0 = (int64_t)r * IT_MACRO;
     c0 = strip * IT_COLS;
     const bool last_half = p.half_last && r == (uint32_t)nmr - 1;  // a 128-row macro row
@@ -1056,9 +1148,21 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     while (v < n_v && !tile_of(v, m0, c0, sub, solo)) ++v;
     return v;
   };
-  const uint32_t vo = (uint32_t)h * 16u * rowbytes + (uint32_t)(8 * L * sizeof(T));
+  const uint32_t vo_lane = (uint32_t)h * 16u * rowbytes + (uint32_t)(8 * L * sizeof(T));
+  // GEN: a lane whose 8 columns lie past K takes an offset beyond every
+  // buffer range (reads zeros, stores nothing); K % 16 == 0, so a lane's
+  // columns are all inside or all past
+  auto lane_vo = [&](int64_t c0) -> uint32_t {
+    if constexpr (GEN) return (c0 + 8 * L < K) ? vo_lane : 0x80000000u;
+    else return vo_lane;
+  };
+  // rows of the wave that exist (GEN: the last macro row may be cut)
+  auto wave_nr = [&](int64_t rs) -> int64_t {
+    if constexpr (GEN) return min(max(p.M - (rs + 32 * wv), (int64_t)0), (int64_t)32);
+    else return 32;
+  };
   auto wave_rows = [&](int64_t rs, int64_t c0) {
-    return make_rsrc(x + (rs + 32 * wv) * K + c0, (int64_t)32 * K * (int64_t)sizeof(T));
+    return make_rsrc(x + (rs + 32 * wv) * K + c0, wave_nr(rs) * K * (int64_t)sizeof(T));
   };
   // grouped tokens: the rows of a sub-step come through a WaveRows map; a
   // lane's row i past its half's n rows gets an offset beyond the buffer's
@@ -1081,7 +1185,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
   // FP32 has none to spare). Loading all 16 rows ahead needs 32 more registers
   // than the 1x16 code has at 2 waves per SIMD and ends up slower; the 2-D
   // code, which cannot start before all 16 rows are in, has them to spare.
-  constexpr int PF = sizeof(T) == 2 ? (B2D ? 16 : 8) : 0;
+  // (the general variant keeps a few more values live per sub-step and
+  // prefetches 4 rows, which keeps it within 256 registers)
+  constexpr int PF = sizeof(T) == 2 ? (B2D ? 16 : (GEN ? 4 : 8)) : 0;
   uint32_t pf[PF > 0 ? PF : 1][NW];
   auto prefetch = [&](int64_t rs, int64_t c0, WaveRows m) {
     if constexpr (PF > 0) {
@@ -1094,6 +1200,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
         // the loads leave ahead of the other wave's arithmetic on the SIMD
         // (not for four-over-six, which is bound by that arithmetic)
         const __amdgpu_buffer_rsrc_t rn = wave_rows(rs, c0);
+        const uint32_t vo = lane_vo(c0);
         if constexpr (VAR != 3) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
         for (int i = 0; i < PF; ++i) load_row_buf<T>(rn, vo, (uint32_t)i * rowbytes, pf[i]);
@@ -1122,14 +1229,16 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     if constexpr (COLW && !B2D) {
       if (GRP || p.col_mode == 2) {
         if (L < 8) {
-          const float a = p.col_amax[rs + 32 * wv + 16 * h];
+          const int64_t gr = rs + 32 * wv + 16 * h;
+          const float a = (!GEN || gr < p.M) ? p.col_amax[gr] : 0.0f;
           sm.ga[wv][h][L] = a;
           sm.gs[wv][h][L] = global_encode_scale(a, p.F);
         }
         __builtin_amdgcn_wave_barrier();
         ctab = ColLds{&sm.ga[wv][h][0], &sm.gs[wv][h][0]};
       } else if (c0 != c0_tab) {
-        const float a = p.col_amax[p.col_mode == 0 ? 0 : c0 + tid];
+        const float a = p.col_mode == 0 ? p.col_amax[0]
+                        : ((!GEN || c0 + tid < K) ? p.col_amax[c0 + tid] : 0.0f);
         __syncthreads();  // every wave is done with the previous strip's table
         sm.ca[tid] = a;
         sm.cs[tid] = global_encode_scale(a, p.F);
@@ -1140,7 +1249,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     // row amax / S_enc of the wave's 32 rows
     if constexpr (ROWW && !B2D) {
       if (lane < 32) {
-        const float a = (p.row_mode == 0) ? p.row_amax[0] : p.row_amax[rs + 32 * wv + lane];
+        const int64_t rr = rs + 32 * wv + lane;
+        const float a = (p.row_mode == 0) ? p.row_amax[0]
+                        : ((!GEN || rr < p.M) ? p.row_amax[rr] : 0.0f);
         sm.ra[wv][lane] = a;
         sm.rs[wv][lane] = global_encode_scale(a, p.F);
       }
@@ -1161,6 +1272,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
       }
     } else {
       const __amdgpu_buffer_rsrc_t rx = wave_rows(rs, c0);
+      const uint32_t vo = lane_vo(c0);
       if constexpr (VAR != 3) __builtin_amdgcn_s_setprio(2);  // as in the prefetch
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -1193,8 +1305,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     st.qc = &sm.qc[mbuf][0][0];
     st.sc = &sm.sc[mbuf][0][0];
     if constexpr (ROWW) {
-      st.qr = make_rsrc(p.q_row + (rs + 32 * wv) * qrs + c0 / 2, (int64_t)32 * qrs);
-      st.vo_qr = (uint32_t)h * 16u * (uint32_t)qrs + (uint32_t)(4 * L);
+      st.qr = make_rsrc(p.q_row + (rs + 32 * wv) * qrs + c0 / 2, wave_nr(rs) * qrs);
+      st.vo_qr = (!GEN || c0 + 8 * L < K) ? (uint32_t)h * 16u * (uint32_t)qrs + (uint32_t)(4 * L)
+                                          : 0x80000000u;
     }
     auto mid = [&]() {
       if constexpr (GRP) {
@@ -1218,16 +1331,58 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) cast_interior_ker
     if constexpr (VAR != 3) __builtin_amdgcn_s_setprio(1);
 
     if constexpr (ROWW) {  // 128 rows x 16 B
-      if (tid < IT_SUB)
-        *reinterpret_cast<uint4*>(p.s_row + (rs + tid) * srs + c0 / 16) =
-            *reinterpret_cast<const uint4*>(&sm.sr[sbuf][tid][0]);
+      if constexpr (GEN) {
+        // the rows that exist, the strip's blocks that exist
+        if (tid < IT_SUB && rs + tid < p.M)
+          store_bytes_any(p.s_row + (rs + tid) * srs + c0 / 16, &sm.sr[sbuf][tid][0], 0,
+                          (int)min((K - c0) / 16, (int64_t)16));
+      } else {
+        if (tid < IT_SUB)
+          *reinterpret_cast<uint4*>(p.s_row + (rs + tid) * srs + c0 / 16) =
+              *reinterpret_cast<const uint4*>(&sm.sr[sbuf][tid][0]);
+      }
     }
     sbuf ^= 1;
     // a half flushed on its own (the last macro row of a matrix with
     // M % 256 = 128, or a split tile of the last round) writes 64 B of codes
     // and 8 scale bytes per column, those of its own 128 rows
     const bool half = cur_solo;
-    if (COLW && (sub == 1 || half)) {
+    if (GEN && COLW && (sub == 1 || half)) {
+      // bytes [lo, hi) of each column's 128 B of codes (a half: its own 64 B;
+      // cut at the column's last byte), to rows of any alignment
+      const int lo = half ? 64 * sub : 0;
+      const int hi = (int)min((int64_t)(half ? lo + 64 : 128), qcs - m0 / 2);
+#pragma unroll
+      for (int it = 0; it < IT_COLS * 8 / 256; ++it) {
+        const int pidx = tid + 256 * it;
+        const int c = pidx >> 3, t = pidx & 7;
+        const int f = (c >> 3) & 15;
+        u32x4 q = *reinterpret_cast<const u32x4*>(&sm.qc[mbuf][c ^ (f & 1)][16 * (t ^ (f >> 1))]);
+        if (f & 1) q = (u32x4){q.z, q.w, q.x, q.y};
+        const uint32_t prev = (uint32_t)__shfl_up((int)q.w, 1, 8);  // S[4t - 1] (t > 0)
+        if (c0 + c < K && hi > lo)
+          store_segment_dwords(p.q_col + (c0 + c) * qcs + m0 / 2, q, prev, t, lo, hi);
+      }
+      // the unaligned bytes at both ends of each column's segment: one
+      // thread per column (byte b of column c sits in slot b / 8, stored at
+      // slot position (b / 8) ^ f of storage column c ^ (f & 1))
+      {
+        const int c = tid, f = (c >> 3) & 15;
+        const uint8_t* col = &sm.qc[mbuf][c ^ (f & 1)][0];
+        if (c0 + c < K && hi > lo)
+          store_segment_ends(p.q_col + (c0 + c) * qcs + m0 / 2, lo, hi, [&](int b) {
+            return col[8 * ((b >> 3) ^ f) + (b & 7)];
+          });
+      }
+      {
+        const int c = 8 * (tid & 31) + (tid >> 5);
+        const int slo = half ? 8 * sub : 0;
+        const int shi = (int)min((int64_t)(half ? slo + 8 : 16), scs - m0 / 16);
+        if (c0 + c < K && shi > slo)
+          store_bytes_any(p.s_col + (c0 + c) * scs + m0 / 16, &sm.sc[mbuf][tid][0], slo, shi);
+      }
+      mbuf ^= 1;
+    } else if (COLW && (sub == 1 || half)) {
       // 256 columns x 128 B of transposed codes: 8 lanes per column, whole
       // lines, slots restored to row order
 #pragma unroll
@@ -1376,7 +1531,7 @@ __global__ void __launch_bounds__(256) cast_edge_kernel(const CastK p) {
   }
 }
 
-template <typename T, bool ROWW, bool COLW, int VAR, bool SPLIT = false>
+template <typename T, bool ROWW, bool COLW, int VAR, bool SPLIT = false, bool GEN = false>
 static int interior_grid() {
   // resident interior workgroups on the device (a multiple of 8), per device
   // (host threads may fill an entry concurrently, with the same value)
@@ -1387,14 +1542,34 @@ static int interior_grid() {
   if (g == 0) {
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW, VAR, SPLIT>), 256, 0) !=
-            hipSuccess ||
+            &per_cu,
+            reinterpret_cast<const void*>(cast_interior_kernel<T, ROWW, COLW, VAR, SPLIT, GEN>),
+            256, 0) != hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     g = std::max(IT_XCDS, (num_cus() * per_cu) / IT_XCDS * IT_XCDS);
     cache[dev].store(g, std::memory_order_relaxed);
   }
   return g;
+}
+
+// General shapes in one launch of the macro-tile kernel (1x16 blocks): every
+// macro tile of the ceil(M / 256) x ceil(K / 256) grid, cut ones included.
+template <typename T, bool ROWW, bool COLW>
+static void launch_cast_general(const CastK& k, hipStream_t s) {
+  const int64_t nt = k.n_istrips * k.n_isteps;
+  const int64_t G0 = interior_grid<T, ROWW, COLW, 0, false, true>();
+  const int64_t per = G0 / IT_XCDS, ntx = (nt + IT_XCDS - 1) / IT_XCDS;
+  const int64_t rounds = (ntx + per - 1) / per;
+  const bool split = per > 0 && rounds > 0 && 2 * (ntx - (rounds - 1) * per) <= per;
+  if (split) {
+    const int64_t G = interior_grid<T, ROWW, COLW, 0, true, true>();
+    hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 0, true, true>), dim3((unsigned)G),
+                       dim3(256), 0, s, k);
+  } else {
+    hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 0, false, true>), dim3((unsigned)G0),
+                       dim3(256), 0, s, k);
+  }
 }
 
 template <typename T, bool ROWW, bool COLW>
@@ -1555,6 +1730,26 @@ static int launch_cast_t(const CastArgs& a, hipStream_t s) {
     k.n_istrips = k.n_isteps = 0;
   if (k.n_istrips == 0 || k.n_isteps == 0) k.n_istrips = k.n_isteps = k.half_last = 0;
   const bool rw = a.q_row != nullptr, cw = a.q_col != nullptr;
+  // Shapes the plain macro-tile path covers alone keep it; every other shape
+  // with 16-byte rows, K % 16 == 0 and plain 1x16 blocks takes the general
+  // variant in one launch (no edge launches).
+  const bool alone = k.n_istrips > 0 && a.M % IT_SUB == 0;
+  const bool general = !alone && a.grp_G == 0 && !a.blk2d && !a.four_six && k.vec_load &&
+                       a.K % 16 == 0 && (int64_t)32 * a.K * (int64_t)sizeof(T) < lim &&
+                       (!a.q_row || (reinterpret_cast<uintptr_t>(a.q_row) & 3) == 0);
+  if (general) {
+    CastK g = k;
+    g.n_istrips = (a.K + IT_COLS - 1) / IT_COLS;
+    g.n_isteps = (a.M + IT_MACRO - 1) / IT_MACRO;
+    const int64_t tail = a.M % IT_MACRO;
+    g.half_last = tail != 0 && tail <= IT_SUB;  // the last macro row has one sub-step
+    if (g.n_isteps * g.n_istrips < ((int64_t)1 << 30)) {
+      if (rw && cw) launch_cast_general<T, true, true>(g, s);
+      else if (rw) launch_cast_general<T, true, false>(g, s);
+      else launch_cast_general<T, false, true>(g, s);
+      return hipGetLastError() == hipSuccess ? 0 : -3;
+    }
+  }
   if (rw && cw && a.four_six) {
     launch_cast_kernels<T, true, false>(k, a, s);
     launch_cast_kernels<T, false, true>(k, a, s);

@@ -102,6 +102,113 @@ def test_fused_amax_ragged_and_fp32(dtype, M, K):
     assert_same("col two-kernel", f32_bits(ca2), f32_bits(ca))
 
 
+# Shapes the general macro-tile variant takes in one launch: ragged M (odd
+# counts included, so transposed code rows have an odd number of bytes),
+# K % 16 == 0 but not a multiple of 256 (a cut last strip), tiny matrices,
+# and M % 128 == 64 (formerly the macro tiles plus a checked launch).
+GENERAL = [
+    (torch.float32, 4097, 2880), (torch.bfloat16, 4097, 2880), (torch.bfloat16, 1, 16),
+    (torch.float32, 1, 16), (torch.bfloat16, 17, 48), (torch.float32, 255, 272),
+    (torch.bfloat16, 257, 4112), (torch.bfloat16, 300, 1040), (torch.float32, 129, 512),
+    (torch.bfloat16, 8256, 512), (torch.float32, 1000, 2000), (torch.bfloat16, 33, 4000),
+    (torch.float32, 383, 784), (torch.bfloat16, 2049, 1296),
+]
+
+
+@pytest.mark.parametrize("dtype,M,K", GENERAL, ids=[f"{d}-{m}x{k}" for d, m, k in GENERAL])
+def test_general_shapes_row_scaled(dtype, M, K):
+    """Row-scaled, both copies, both bounds, dequantized both ways: every byte
+    and bit against the oracle. Values over a wide exponent range (FP32
+    subnormals included), with zero rows and columns planted."""
+    g = torch.Generator().manual_seed(M * 31 + K)
+    e = torch.randint(-135 if dtype == torch.float32 else -125, 100, (M, 1), generator=g).float()
+    x = torch.randn(M, K, generator=g) * torch.pow(2.0, e)
+    x[M // 2] = 0.0
+    x[:, K // 3] = 0.0
+    x = x.to(dtype)
+    assert torch.isfinite(x.float()).all()
+    check_row_scaled(x, bounds=(448.0, 256.0), label=f"general {M}x{K}")
+
+
+@pytest.mark.parametrize("dtype,M,K", [(torch.float32, 4097, 2880), (torch.bfloat16, 257, 1040),
+                                       (torch.bfloat16, 129, 48)])
+@pytest.mark.parametrize("rowwise,colwise", [(True, False), (False, True)])
+def test_general_shapes_one_direction(dtype, M, K, rowwise, colwise):
+    say(f"[gpu] general {M}x{K} {dtype} rowwise={rowwise} colwise={colwise}")
+    g = torch.Generator().manual_seed(M + 3 * K)
+    x = (torch.randn(M, K, generator=g) * torch.exp(torch.randn(M, 1, generator=g) * 4)).to(dtype)
+    xf = x.float().numpy()
+    xd = x.to(DEV)
+    ra, ca, _ = gpu_amax(xd)
+    out = gpu_quantize(xd, 1, ra, 1, ca, 448.0, rowwise=rowwise, colwise=colwise)
+    if rowwise:
+        qr, sr = oracle.quantize_rowwise(xf, oracle.MODE_LINE, oracle.amax_rows(xf), 448.0)
+        assert_same("q_row", to_np(out["q_row"]), qr)
+        assert_same("s_row", to_np(out["s_row"]), sr)
+    else:
+        qc, sc = oracle.quantize_colwise(xf, oracle.MODE_LINE, oracle.amax_cols(xf), 448.0)
+        assert_same("q_col", to_np(out["q_col"]), qc)
+        assert_same("s_col", to_np(out["s_col"]), sc)
+
+
+@pytest.mark.parametrize("dtype,M,K", [(torch.float32, 4097, 2880), (torch.bfloat16, 401, 528)])
+def test_general_shapes_tensor_and_rowgroup_modes(dtype, M, K):
+    """Per-tensor amax in both directions, and the row-group column mode
+    (block b of a column takes amax[16 b]) with cut blocks at the bottom."""
+    say(f"[gpu] general {M}x{K} {dtype} tensor / rowgroup modes")
+    g = torch.Generator().manual_seed(M + K + 1)
+    x = (torch.randn(M, K, generator=g) * 10.0).to(dtype)
+    xf = x.float().numpy()
+    xd = x.to(DEV)
+    _, _, ta = gpu_amax(xd, row=False, col=False, tensor=True)
+    out = gpu_quantize(xd, 0, ta, 0, ta, 256.0)
+    t = float(oracle.amax_tensor(xf))
+    qr, sr = oracle.quantize_rowwise(xf, oracle.MODE_TENSOR, t, 256.0)
+    qc, sc = oracle.quantize_colwise(xf, oracle.MODE_TENSOR, t, 256.0)
+    for name, got, want in (("q_row", out["q_row"], qr), ("s_row", out["s_row"], sr),
+                            ("q_col", out["q_col"], qc), ("s_col", out["s_col"], sc)):
+        assert_same(name, to_np(got), want)
+    ends = np.array([16 * 5, 16 * 9, M], dtype=np.int64)
+    ga = oracle.group_amax_expand(oracle.amax_rows(xf), ends)
+    gad = torch.from_numpy(ga).to(DEV)
+    out = gpu_quantize(xd, 1, gad, 2, gad, 448.0)
+    qr, sr = oracle.quantize_rowwise(xf, oracle.MODE_LINE, ga, 448.0)
+    qc, sc = oracle.quantize_colwise(xf, oracle.MODE_ROWGROUP, ga, 448.0)
+    for name, got, want in (("q_row", out["q_row"], qr), ("s_row", out["s_row"], sr),
+                            ("q_col", out["q_col"], qc), ("s_col", out["s_col"], sc)):
+        assert_same(name + " rowgroup", to_np(got), want)
+
+
+@pytest.mark.parametrize("shift", [1, 2, 3, 5])
+def test_general_shapes_outputs_at_odd_offsets(shift):
+    """Transposed codes and both scale copies starting at odd byte offsets
+    (views into larger buffers): every row start has another alignment, and
+    nothing outside the outputs' bytes is written."""
+    M, K = 259, 528
+    say(f"[gpu] general {M}x{K} outputs shifted by {shift} bytes")
+    g = torch.Generator().manual_seed(shift)
+    x = (torch.randn(M, K, generator=g) * 3.0).to(torch.bfloat16)
+    xf = x.float().numpy()
+    xd = x.to(DEV)
+    ra, ca, _ = gpu_amax(xd)
+    sizes = {"q_row": M * (K // 2), "s_row": M * (K // 16), "q_col": K * ((M + 1) // 2),
+             "s_col": K * ((M + 15) // 16)}
+    bufs, views = {}, {}
+    for name, n in sizes.items():
+        sh = 4 * shift if name == "q_row" else shift  # rowwise codes: dword-aligned rows
+        bufs[name] = torch.full((n + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+        views[name] = bufs[name][sh:sh + n]
+    p.nvfp4_quantize_transpose(xd, 1, ra, 1, ca, 448.0, views["q_row"], views["s_row"],
+                               views["q_col"], views["s_col"])
+    qr, sr = oracle.quantize_rowwise(xf, oracle.MODE_LINE, oracle.amax_rows(xf), 448.0)
+    qc, sc = oracle.quantize_colwise(xf, oracle.MODE_LINE, oracle.amax_cols(xf), 448.0)
+    for name, want in (("q_row", qr), ("s_row", sr), ("q_col", qc), ("s_col", sc)):
+        b = to_np(bufs[name])
+        sh = 4 * shift if name == "q_row" else shift
+        assert_same(name, b[sh:sh + sizes[name]], want.ravel())
+        assert (b[:sh] == 0xA5).all() and (b[sh + sizes[name]:] == 0xA5).all(), name
+
+
 @pytest.mark.parametrize("M,K", [(128, 256), (384, 768), (640, 256), (192, 512), (448, 512)])
 def test_interior_half_macro_tiles(M, K):
     """M % 256 = 128 or 192: the interior kernel's last macro row is a 128-row
