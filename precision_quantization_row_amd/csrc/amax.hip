@@ -55,15 +55,15 @@ __global__ void __launch_bounds__(256) amax_init_kernel(float* ra, int64_t M, fl
 // BF16, K % 4 == 0 for FP32) with a 16-byte aligned X: a lane's 16-byte
 // vector lies wholly inside the row or wholly past its end (then it reads
 // nothing and counts as zeros), and rows past M are skipped.
-constexpr int FUSED_NC = 4;    // chunks per tile -> 512 BF16 / 256 FP32 columns
 constexpr int FUSED_TR = 256;  // rows per tile (largest)
-constexpr int FUSED_RU = 2;    // rows per slot per loop iteration
 
-template <typename T>
+// NC chunks per tile (the tile width), RU rows per slot per loop iteration:
+// NC * RU 16-byte loads in flight per lane.
+template <typename T, int NC>
 struct FusedGeom {
   static constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
   static constexpr int CH = 16 * V;         // columns per chunk
-  static constexpr int TC = CH * FUSED_NC;  // columns per tile
+  static constexpr int TC = CH * NC;        // columns per tile
 };
 
 // Magnitude bits of one dword's elements, maxed into acc (BF16: two packed
@@ -81,14 +81,14 @@ __device__ __forceinline__ uint32_t mag_bits(uint32_t acc) {
   else return acc;
 }
 
-template <typename T>
+template <typename T, int FUSED_NC, int FUSED_RU>
 __global__ void __launch_bounds__(256) fused_amax_kernel(const T* __restrict__ x, int64_t M,
                                                          int64_t K, float* __restrict__ ra,
                                                          float* __restrict__ ca,
                                                          const float* noop, int64_t tiles_c,
                                                          int64_t tr) {
   if (skip(noop)) return;
-  using G = FusedGeom<T>;
+  using G = FusedGeom<T, FUSED_NC>;
   __shared__ uint32_t colmax_s[16][FUSED_NC * 64 + 1];
   __shared__ uint32_t rowmax_s[FUSED_TR];  // the tile's row maxima, published at the end
   const int tid = threadIdx.x;
@@ -524,19 +524,38 @@ int launch_amax_init(float* ra, int64_t M, float* ca, int64_t K, float* ta, cons
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+template <typename T, int NC, int RU>
+static int launch_fused_nc(const void* x, int64_t M, int64_t K, float* ra, float* ca,
+                           const float* noop, hipStream_t s, int64_t tr_min) {
+  const int64_t tiles_c = (K + FusedGeom<T, NC>::TC - 1) / FusedGeom<T, NC>::TC;
+  // Tall tiles publish fewer column maxima; short ones give more workgroups.
+  // Take the tallest tile (256 .. tr_min rows) that still gives about 6
+  // workgroups per CU.
+  int64_t tr = FUSED_TR;
+  while (tr > tr_min && ((M + tr - 1) / tr) * tiles_c < (int64_t)num_cus() * 6) tr /= 2;
+  const int64_t tiles_r = (M + tr - 1) / tr;
+  hipLaunchKernelGGL((fused_amax_kernel<T, NC, RU>), dim3((unsigned)(tiles_r * tiles_c)),
+                     dim3(256), 0, s, static_cast<const T*>(x), M, K, ra, ca, noop, tiles_c, tr);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// Tile shape per matrix. Large matrices (256-row tiles of 4 chunks already
+// give 6 workgroups per CU) and tiny ones keep 4-chunk tiles. In between,
+// 128-column tiles of 128 rows or more (1 BF16 / 2 FP32 chunks, 8 loads in
+// flight per lane) publish about half as many atomics as 512-column tiles cut
+// to 32 rows for the same workgroup count: 4096 x 4096 BF16 7.2 us against
+// 10.1 (amax pass back to back), FP32 4097 x 2880 the same or better.
 template <typename T>
 static int launch_fused_t(const void* x, int64_t M, int64_t K, float* ra, float* ca,
                           const float* noop, hipStream_t s) {
-  const int64_t tiles_c = (K + FusedGeom<T>::TC - 1) / FusedGeom<T>::TC;
-  // Tall tiles publish fewer column maxima; short ones give more workgroups.
-  // Take the tallest tile (256 .. 32 rows) that still gives about 6
-  // workgroups per CU.
-  int64_t tr = FUSED_TR;
-  while (tr > 32 && ((M + tr - 1) / tr) * tiles_c < (int64_t)num_cus() * 6) tr /= 2;
-  const int64_t tiles_r = (M + tr - 1) / tr;
-  hipLaunchKernelGGL(fused_amax_kernel<T>, dim3((unsigned)(tiles_r * tiles_c)), dim3(256), 0, s,
-                     static_cast<const T*>(x), M, K, ra, ca, noop, tiles_c, tr);
-  return hipGetLastError() == hipSuccess ? 0 : -3;
+  const int64_t cus = num_cus();
+  const int64_t t4 = (K + FusedGeom<T, 4>::TC - 1) / FusedGeom<T, 4>::TC;
+  if (((M + FUSED_TR - 1) / FUSED_TR) * t4 >= cus * 6)
+    return launch_fused_nc<T, 4, 2>(x, M, K, ra, ca, noop, s, 32);
+  constexpr int NN = sizeof(T) == 2 ? 1 : 2, RN = 8 / NN;
+  const int64_t tn = (K + FusedGeom<T, NN>::TC - 1) / FusedGeom<T, NN>::TC;
+  if (((M + 127) / 128) * tn >= cus * 2) return launch_fused_nc<T, NN, RN>(x, M, K, ra, ca, noop, s, 128);
+  return launch_fused_nc<T, 4, 2>(x, M, K, ra, ca, noop, s, 32);
 }
 
 int launch_fused_amax(const void* x, int in_dtype, int64_t M, int64_t K, float* ra, float* ca,

@@ -76,7 +76,9 @@ def test_fused_amax_tile_heights(M, K):
     (torch.float32, 4097, 2880), (torch.float32, 1, 4), (torch.float32, 17, 260),
     (torch.float32, 300, 1028), (torch.float32, 33, 65540 // 4 * 4), (torch.float32, 1000, 12),
     (torch.bfloat16, 1, 8), (torch.bfloat16, 257, 520), (torch.bfloat16, 129, 4104),
-    (torch.bfloat16, 4097, 2888), (torch.bfloat16, 70, 24)])
+    (torch.bfloat16, 4097, 2888), (torch.bfloat16, 70, 24),
+    # the 128-column tiles of medium matrices, with a cut last chunk
+    (torch.bfloat16, 2000, 4104), (torch.float32, 3000, 5000)])
 def test_fused_amax_ragged_and_fp32(dtype, M, K):
     """The one-pass amax on shapes outside the 128-aligned BF16 case: FP32,
     ragged M, and K that ends inside a chunk or a tile (only whole 16-byte
