@@ -22,13 +22,15 @@ the whole region before the GPU reaches it. Also reported: the dequantize
 kernel's bandwidth, the other kernels of the path on the workloads they serve
 (two-kernel and per-tensor amax, 2-D tiles, four-over-six, quantize +
 dequantize, the FP32 edge matrix, grouped tokens, and the two small matrices
-cold and warm), the fused-amax PR's comparison (whole quantize with the fused
+cold and warm; the 2-D tile cast also as a whole step, per-tensor amax pass
+then cast, timed like the headline step), the fused-amax PR's comparison (whole quantize with the fused
 amax against the separate row and column amax kernels, medians), what plain
 streaming kernels sustain on the same GPU (read, write, copy), and the CPU
 oracle timed on a bounded sample of the same workload on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
        python bench.py --copy-calibration   (plain torch copy, for counter scaling)
+       python bench.py --case 2d [--case grouped ...]   (those rows alone, for profiling)
 """
 from __future__ import annotations
 
@@ -198,61 +200,122 @@ def cold_warm(torch, ref, fn, nbytes, hold, calls=2, reps=20):
     return out
 
 
-def other_rows(p, workloads, torch, dev, xs, timed, bound, ref, hold):
-    """The remaining kernels of the path, each on the workload it serves,
-    timed alone (back-to-back launches, events at the region's ends). Bytes
-    are those each launch actually has to move (the two-kernel amax reads X
-    twice)."""
-    n = 20
-    res = {}
-    x = xs[0]
-    M, K = x.shape
+class Ctx:
+    """What every case below needs: the package, torch, the device, the two
+    copies of the headline matrix, the timers and the streaming reference."""
+
+    def __init__(self, p, workloads, torch, dev, xs, timed, bound, ref, hold):
+        self.p, self.workloads, self.torch, self.dev = p, workloads, torch, dev
+        self.xs, self.timed, self.bound, self.ref, self.hold = xs, timed, bound, ref, hold
+
+    def events(self, n):
+        ev = self.torch.cuda.Event
+        return [(ev(enable_timing=True), ev(enable_timing=True)) for _ in range(n)]
+
+
+N_ROW = 20  # launches (or steps) per region in the cases below
+
+
+def case_amax(c):
+    """Two-kernel and per-tensor amax on the headline matrix."""
+    p, torch, dev, xs = c.p, c.torch, c.dev, c.xs
+    M, K = xs[0].shape
     ra = torch.empty(M, dtype=torch.float32, device=dev)
     ca = torch.empty(K, dtype=torch.float32, device=dev)
     ta = torch.empty(1, dtype=torch.float32, device=dev)
     xb = M * K * 2
+    res = {}
     f2 = lambda i: p.nvfp4_amax_rowcol(xs[i & 1], ra, ca, flags=p.NVFP4_FLAG_FORCE_TWO_KERNEL)
     f2(0)
-    res["two_kernel_amax_bf16_8192x28672"] = _row(timed(f2, n) * 1e3, 2 * xb + 4 * (M + K),
+    res["two_kernel_amax_bf16_8192x28672"] = _row(c.timed(f2, N_ROW) * 1e3, 2 * xb + 4 * (M + K),
                                                   "X read by each of the two kernels, vectors written")
     ft = lambda i: p.nvfp4_amax_rowcol(xs[i & 1], None, None, tensor_amax=ta)
     ft(0)
-    res["tensor_amax_bf16_8192x28672"] = _row(timed(ft, n) * 1e3, xb + 4, "X read once")
-    # 2-D 16 x 16 tile scales, both copies, on the same matrix (per-tensor amax
-    # already in ta)
+    res["tensor_amax_bf16_8192x28672"] = _row(c.timed(ft, N_ROW) * 1e3, xb + 4, "X read once")
+    return res
+
+
+def case_2d(c):
+    """2-D 16 x 16 tile scales, both copies, on the headline matrix: the cast
+    back to back, and the whole 2-D quantize step (per-tensor amax pass, then
+    the cast) measured like the headline step."""
+    p, torch, dev, xs = c.p, c.torch, c.dev, c.xs
+    M, K = xs[0].shape
+    xb = M * K * 2
+    ta = torch.empty(1, dtype=torch.float32, device=dev)
     out = p.empty_outputs(M, K, dev)
-    f2d = lambda i: p.nvfp4_quantize_2d(xs[i & 1], ta, bound, out["q_row"], out["s_row"],
+    amax = lambda i: p.nvfp4_amax_rowcol(xs[i & 1], None, None, tensor_amax=ta)
+    f2d = lambda i: p.nvfp4_quantize_2d(xs[i & 1], ta, c.bound, out["q_row"], out["s_row"],
                                         out["q_col"], out["s_col"])
+    amax(0)
     f2d(0)
     cb2 = xb + 4 + 2 * (M * (K // 2) + M * (K // 16))
-    res["quantize_2d_bf16_8192x28672"] = _row(timed(f2d, n) * 1e3, cb2,
-                                              "X read once, both copies written")
-    del out
-    # four-over-six block scales, both copies (row and column amax given;
-    # one launch per direction, so X is read twice)
+    res = {"quantize_2d_bf16_8192x28672": _row(
+        c.timed(f2d, N_ROW) * 1e3, cb2,
+        "X read once, both copies written; back to back, each launch also absorbing the previous "
+        "launch's write-back")}
+    # the step: whole steps with events at the region's ends, then the same
+    # steps with an event pair around each cast
+    step_ms = c.timed(lambda i: (amax(i), f2d(i)), N_ROW, 2)
+    ev = c.events(N_ROW)
+    torch.cuda.synchronize()
+    c.hold(4 * N_ROW)
+    for i in range(N_ROW):
+        amax(i)
+        ev[i][0].record()
+        f2d(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    cast_ms = sum(a.elapsed_time(b) for a, b in ev) / N_ROW
+    row = _row(step_ms * 1e3, xb + 4 + cb2,
+               "X read by the per-tensor amax pass and the cast, both copies written")
+    cast = _row(cast_ms * 1e3, cb2, "the cast launch inside the step, event pair around it")
+    row.update({"cast_in_step_us": cast["us"], "cast_in_step_GBs": cast["GBs"],
+                "cast_in_step_frac": cast["frac"]})
+    res["quantize_2d_step_bf16_8192x28672"] = row
+    return res
+
+
+def case_4over6(c):
+    """Four-over-six block scales, both copies (row and column amax given; one
+    launch per direction, so X is read twice)."""
+    p, torch, dev, xs = c.p, c.torch, c.dev, c.xs
+    M, K = xs[0].shape
+    xb = M * K * 2
+    ra = torch.empty(M, dtype=torch.float32, device=dev)
+    ca = torch.empty(K, dtype=torch.float32, device=dev)
     p.nvfp4_amax_rowcol(xs[0], ra, ca)
     out = p.empty_outputs(M, K, dev)
     f46 = lambda i: p.nvfp4_quantize_4over6(xs[i & 1], p.NVFP4_AMAX_LINE, ra, p.NVFP4_AMAX_LINE, ca,
                                             256.0, out["q_row"], out["s_row"], out["q_col"],
                                             out["s_col"])
     f46(0)
-    res["quantize_4over6_bf16_8192x28672"] = _row(
-        timed(f46, 5) * 1e3, 2 * xb + 4 * (M + K) + 2 * (M * (K // 2) + M * (K // 16)),
-        "X read once per direction, both copies written")
-    del out
-    # rowwise codes and their BF16 dequantization in one pass (row amax given)
+    return {"quantize_4over6_bf16_8192x28672": _row(
+        c.timed(f46, 5) * 1e3, 2 * xb + 4 * (M + K) + 2 * (M * (K // 2) + M * (K // 16)),
+        "X read once per direction, both copies written")}
+
+
+def case_qdq(c):
+    """Rowwise codes and their BF16 dequantization in one pass (row amax given)."""
+    p, torch, dev, xs = c.p, c.torch, c.dev, c.xs
+    M, K = xs[0].shape
+    ra = torch.empty(M, dtype=torch.float32, device=dev)
     p.nvfp4_amax_rowcol(xs[0], ra)
     qr = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
     sr = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
     yq = torch.empty(M, K, dtype=torch.bfloat16, device=dev)
-    fq = lambda i: p.nvfp4_quantize_dequantize(xs[i & 1], p.NVFP4_AMAX_LINE, ra, bound, yq, qr, sr)
+    fq = lambda i: p.nvfp4_quantize_dequantize(xs[i & 1], p.NVFP4_AMAX_LINE, ra, c.bound, yq, qr, sr)
     fq(0)
-    res["quantize_dequantize_bf16_8192x28672"] = _row(
-        timed(fq, n) * 1e3, xb + 4 * M + M * (K // 2) + M * (K // 16) + M * K * 2,
-        "X read once, rowwise codes + scales and the BF16 operand written")
-    del qr, sr, yq
+    return {"quantize_dequantize_bf16_8192x28672": _row(
+        c.timed(fq, N_ROW) * 1e3, M * K * 2 + 4 * M + M * (K // 2) + M * (K // 16) + M * K * 2,
+        "X read once, rowwise codes + scales and the BF16 operand written")}
 
-    w = workloads.make("fp32_edge")
+
+def case_fp32_edge(c):
+    """The FP32 4097 x 2880 matrix: amax (one-pass and two-kernel), cast, and
+    the whole quantize back to back, cold and warm."""
+    p, torch, dev, wl = c.p, c.torch, c.dev, c.workloads
+    w = wl.make("fp32_edge")
     M, K = w.shape
     x = w.x.to(dev)
     ra = torch.empty(M, dtype=torch.float32, device=dev)
@@ -260,67 +323,83 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound, ref, hold):
     out = p.empty_outputs(M, K, dev)
     fa = lambda i: p.nvfp4_amax_rowcol(x, ra, ca)
     fa2 = lambda i: p.nvfp4_amax_rowcol(x, ra, ca, flags=p.NVFP4_FLAG_FORCE_TWO_KERNEL)
-    fc = lambda i: p.nvfp4_quantize_transpose(x, 1, ra, 1, ca, bound, out["q_row"], out["s_row"],
+    fc = lambda i: p.nvfp4_quantize_transpose(x, 1, ra, 1, ca, c.bound, out["q_row"], out["s_row"],
                                               out["q_col"], out["s_col"])
     fa(0); fa2(0); fc(0)
     assert p.nvfp4_amax_path(p.NVFP4_FP32, M, K, 1, 1, 0) == 1  # one-pass amax
     cb = M * K * 4 + 4 * (M + K) + M * ((K + 1) // 2) + M * ((K + 15) // 16) + K * ((M + 1) // 2) \
         + K * ((M + 15) // 16)
-    res["fp32_4097x2880_amax"] = _row(timed(fa, n) * 1e3, M * K * 4 + 4 * (M + K),
+    res = {}
+    res["fp32_4097x2880_amax"] = _row(c.timed(fa, N_ROW) * 1e3, M * K * 4 + 4 * (M + K),
                                       "one-pass row + column amax: X read once, vectors written")
-    res["fp32_4097x2880_two_kernel_amax"] = _row(timed(fa2, n) * 1e3, 2 * M * K * 4 + 4 * (M + K),
+    res["fp32_4097x2880_two_kernel_amax"] = _row(c.timed(fa2, N_ROW) * 1e3,
+                                                 2 * M * K * 4 + 4 * (M + K),
                                                  "X read by each of the two kernels (forced)")
-    res["fp32_4097x2880_cast"] = _row(timed(fc, n) * 1e3, cb, "X read once, both copies written")
+    res["fp32_4097x2880_cast"] = _row(c.timed(fc, N_ROW) * 1e3, cb, "X read once, both copies written")
     fac = lambda i: (fa(i), fc(i))
     res["fp32_4097x2880_amax_and_cast"] = _row(
-        timed(fac, n, 2) * 1e3, workloads.algorithmic_bytes(M, K, 4),
+        c.timed(fac, N_ROW, 2) * 1e3, wl.algorithmic_bytes(M, K, 4),
         "the whole quantize (one-pass amax, then cast), back to back; algorithmic bytes "
         "(X counted twice)")
     res["fp32_4097x2880_amax_and_cast"].update(
-        cold_warm(torch, ref, lambda: fac(0), workloads.algorithmic_bytes(M, K, 4), hold))
-    del x, out
+        cold_warm(torch, c.ref, lambda: fac(0), wl.algorithmic_bytes(M, K, 4), c.hold))
+    return res
 
-    w = workloads.make("moe_groups")
+
+def case_grouped(c):
+    """Grouped tokens (16 groups of about 1024 rows x 4096, padded to 128
+    rows): the three-call sequence on the padded layout, and the one-call
+    grouped quantize from the token rows."""
+    p, torch, dev = c.p, c.torch, c.dev
+    w = c.workloads.make("moe_groups")
     M, K = w.shape
     x = w.x.to(dev)
     ge = w.group_end.to(dev)
     ra = torch.empty(M, dtype=torch.float32, device=dev)
     out = p.empty_outputs(M, K, dev)
+
     def moe(i):
         # per-group amax: row amax expanded over each group, colwise blocks use
         # the group amax of their rows
         p.nvfp4_amax_rowcol(x, ra)
         p.nvfp4_group_amax_expand(ra, ge)
-        p.nvfp4_quantize_transpose(x, 1, ra, 2, ra, bound, out["q_row"], out["s_row"],
+        p.nvfp4_quantize_transpose(x, 1, ra, 2, ra, c.bound, out["q_row"], out["s_row"],
                                    out["q_col"], out["s_col"])
+
     moe(0)
     mb = 2 * M * K * 2 + 4 * 4 * M + 8 * ge.numel() + M * ((K + 1) // 2) + M * ((K + 15) // 16) \
         + K * ((M + 1) // 2) + K * ((M + 15) // 16)
-    res["moe_%dx%d_amax_expand_cast" % (M, K)] = _row(timed(moe, n, 3) * 1e3, mb,
-                                                       "X read by the amax and the cast passes")
+    res = {"moe_%dx%d_amax_expand_cast" % (M, K): _row(c.timed(moe, N_ROW, 3) * 1e3, mb,
+                                                        "X read by the amax and the cast passes")}
     del x
-
     # the same groups as token rows, padded on the way in by one call
     starts = torch.cat([torch.zeros(1, dtype=torch.int64), w.group_end[:-1]])
     tok = torch.cat([w.x[int(s):int(s) + int(r)] for s, r in zip(starts, w.group_rows)]).to(dev)
     T = tok.shape[0]
     gr = w.group_rows.to(dev)
+
     def grouped(i):
-        p.nvfp4_quantize_grouped(tok, gr, 128, M, bound, ra, out["q_row"], out["s_row"],
+        p.nvfp4_quantize_grouped(tok, gr, 128, M, c.bound, ra, out["q_row"], out["s_row"],
                                  out["q_col"], out["s_col"])
+
     grouped(0)
     gb = 2 * T * K * 2 + 4 * M + 8 * gr.numel() + M * ((K + 1) // 2) + M * ((K + 15) // 16) \
         + K * ((M + 1) // 2) + K * ((M + 15) // 16)
     res["moe_%dtok_x%d_quantize_grouped" % (T, K)] = _row(
-        timed(grouped, n) * 1e3, gb, "token rows read by the amax and the cast, padded layout written")
-    del tok, out
+        c.timed(grouped, N_ROW) * 1e3, gb,
+        "token rows read by the amax and the cast, padded layout written")
+    return res
 
-    # the two small matrices, one whole quantize each (amax pass + cast):
-    # median of 20 cold repetitions (the memory-side cache evicted by a
-    # read-only pass before each) and of 20 warm ones (the same call again
-    # right after itself); the 256 x 256 case is launch-bound
+
+def case_small(c):
+    """The two small matrices, one whole quantize each (amax pass + cast):
+    median of 20 cold repetitions (the memory-side cache evicted by a
+    read-only pass before each) and of 20 warm ones (the same call again right
+    after itself); the 256 x 256 case is launch-bound."""
+    p, torch, dev, wl = c.p, c.torch, c.dev, c.workloads
+    res = {}
     for name in ("tiny_rowscale", "outliers"):
-        w = workloads.make(name)
+        w = wl.make(name)
         M, K = w.shape
         x = w.x.to(dev)
         ra = torch.empty(M, dtype=torch.float32, device=dev)
@@ -330,22 +409,36 @@ def other_rows(p, workloads, torch, dev, xs, timed, bound, ref, hold):
 
         def row_scaled():
             p.nvfp4_amax_rowcol(x, ra, ca)
-            p.nvfp4_quantize_transpose(x, 1, ra, 1, ca, bound, out["q_row"], out["s_row"],
+            p.nvfp4_quantize_transpose(x, 1, ra, 1, ca, c.bound, out["q_row"], out["s_row"],
                                        out["q_col"], out["s_col"])
 
         def per_tensor():
             p.nvfp4_amax_rowcol(x, None, None, tensor_amax=ta)
-            p.nvfp4_quantize_transpose(x, 0, ta, 0, ta, bound, out["q_row"], out["s_row"],
+            p.nvfp4_quantize_transpose(x, 0, ta, 0, ta, c.bound, out["q_row"], out["s_row"],
                                        out["q_col"], out["s_col"])
 
         res["%s_%dx%d_row_scaled" % (name, M, K)] = cold_warm(
-            torch, ref, row_scaled, workloads.algorithmic_bytes(M, K, 2), hold)
+            torch, c.ref, row_scaled, wl.algorithmic_bytes(M, K, 2), c.hold)
         if name == "outliers":
             res["%s_%dx%d_per_tensor" % (name, M, K)] = cold_warm(
-                torch, ref, per_tensor,
-                workloads.algorithmic_bytes(M, K, 2, row_amax=False, col_amax=False,
-                                            tensor_amax=True), hold)
+                torch, c.ref, per_tensor,
+                wl.algorithmic_bytes(M, K, 2, row_amax=False, col_amax=False,
+                                     tensor_amax=True), c.hold)
         del x, out
+    return res
+
+
+CASES = {"amax": case_amax, "2d": case_2d, "4over6": case_4over6, "qdq": case_qdq,
+         "fp32_edge": case_fp32_edge, "grouped": case_grouped, "small": case_small}
+
+
+def other_rows(ctx, names=None):
+    """The remaining kernels of the path, each on the workload it serves.
+    Back-to-back regions have events at their ends only; bytes are those each
+    launch actually has to move (the two-kernel amax reads X twice)."""
+    res = {}
+    for name in (names or CASES):
+        res.update(CASES[name](ctx))
     return res
 
 
@@ -365,6 +458,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time the CPU oracle is run for (whole passes)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--case", action="append", choices=sorted(CASES),
+                    help="run only this case of the other rows (repeatable), after the warm-up; "
+                         "prints their rows alone")
     ap.add_argument("--hold-ms", type=float, default=None,
                     help="length of the spin kernel queued ahead of each timed region "
                          "(default: 1 ms + 1.5 x the host's measured time to enqueue it)")
@@ -472,6 +568,15 @@ def main():
     host_ms_per_call[0] = (time.perf_counter() - t_host) * 1e3 / 8
     torch.cuda.synchronize()
 
+    if args.case:
+        # only the named cases (for a profiler run): no headline, no streaming
+        # reference, no CPU baseline
+        ctx = Ctx(p, workloads, torch, dev, xs, timed, bound, StreamRef(torch, dev), hold_queue)
+        print(json.dumps({"cases": args.case, "rows": other_rows(ctx, args.case),
+                          "source_digest": source_digest(),
+                          "library": os.path.relpath(p.library_path(), ROOT)}))
+        return
+
     K_steps = args.steps
     step_bytes = workloads.algorithmic_bytes(M, K, 2)
     # headline: K whole steps
@@ -539,8 +644,8 @@ def main():
     dq_bytes = M * ((K + 1) // 2) + M * ((K + 15) // 16) + 4 * M + M * K * 2
     del y
 
-    row_meas = {} if args.no_rows else other_rows(p, workloads, torch, dev, xs, timed, bound, ref,
-                                                        hold_queue)
+    row_meas = {} if args.no_rows else other_rows(
+        Ctx(p, workloads, torch, dev, xs, timed, bound, ref, hold_queue))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -182,12 +182,15 @@ def test_macro_tile_layouts(dtype, case):
         group_rows = [40, 90]
     T = sum(group_rows) if T is None else T
     x = _tokens(T, K, dtype, seed=len(case) + K)
-    m_out = _round64(_full_rows(group_rows, align))
-    if case == "truncated":
-        m_out = 512
-    if case == "past":
-        m_out += 256
-    _check(case, x, group_rows, align, m_out)
+    # M_out a multiple of 64 (the last macro-tile sub-step half full) and of
+    # 128 (every sub-step full)
+    for rnd in (64, 128):
+        m_out = -(-_full_rows(group_rows, align) // rnd) * rnd
+        if case == "truncated":
+            m_out = 512 - 64 * (rnd == 64)
+        if case == "past":
+            m_out += 256
+        _check(f"{case} M_out {m_out}", x, group_rows, align, m_out)
     if case == "mixed" and dtype == torch.bfloat16:
         _check("mixed rowwise", x, group_rows, align, m_out, colwise=False)
         _check("mixed colwise", x, group_rows, align, m_out, rowwise=False)
