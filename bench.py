@@ -254,19 +254,21 @@ def case_2d(c):
         c.timed(f2d, N_ROW) * 1e3, cb2,
         "X read once, both copies written; back to back, each launch also absorbing the previous "
         "launch's write-back")}
-    # the step: whole steps with events at the region's ends, then the same
-    # steps with an event pair around each cast
-    step_ms = c.timed(lambda i: (amax(i), f2d(i)), N_ROW, 2)
-    ev = c.events(N_ROW)
+    # the step: whole steps with events at the region's ends (200 of them: a
+    # region pays a fixed cost where it starts), then the same steps with an
+    # event pair around each cast
+    n = 200
+    step_ms = c.timed(lambda i: (amax(i), f2d(i)), n, 2)
+    ev = c.events(n)
     torch.cuda.synchronize()
-    c.hold(4 * N_ROW)
-    for i in range(N_ROW):
+    c.hold(4 * n)
+    for i in range(n):
         amax(i)
         ev[i][0].record()
         f2d(i)
         ev[i][1].record()
     torch.cuda.synchronize()
-    cast_ms = sum(a.elapsed_time(b) for a, b in ev) / N_ROW
+    cast_ms = sum(a.elapsed_time(b) for a, b in ev) / n
     row = _row(step_ms * 1e3, xb + 4 + cb2,
                "X read by the per-tensor amax pass and the cast, both copies written")
     cast = _row(cast_ms * 1e3, cb2, "the cast launch inside the step, event pair around it")

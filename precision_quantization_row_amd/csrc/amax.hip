@@ -352,11 +352,20 @@ __global__ void __launch_bounds__(TENSOR_THREADS) tensor_amax_kernel(const T* __
     const uint4* xv = reinterpret_cast<const uint4*>(x);
     const int64_t nv = n / V;
     // a wave reads 64 x 16 B per load; four loads of consecutive 1 KB pieces
-    // are in flight per wave and iteration
+    // are in flight per wave and iteration. The first two pieces stream past
+    // the caches (non-temporal) and the last two are read normally, so the
+    // cast that reads X next finds half of it in the memory-side cache
+    // without this pass evicting that half. Measured on 8192 x 28672 BF16
+    // (same GPU, per-tensor amax + 2-D cast per step): all pieces cached
+    // 208.0 us per step (this pass alone 80.6 us), all streamed 207.2 (72.7),
+    // half and half 194.3 (74.1).
     const int64_t lane = threadIdx.x & 63, wave = t0 >> 6, nwaves = stride >> 6;
     int64_t i = wave * 256 + lane;
     for (; i + 192 < nv; i += nwaves * 256) {
-      const uint4 a = xv[i], b = xv[i + 64], c = xv[i + 128], d = xv[i + 192];
+      const u32x4 sa = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xv + i));
+      const u32x4 sb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xv + i + 64));
+      const uint4 a = make_uint4(sa.x, sa.y, sa.z, sa.w), b = make_uint4(sb.x, sb.y, sb.z, sb.w);
+      const uint4 c = xv[i + 128], d = xv[i + 192];
       m = max(m, max(max(vec_max_bits<T>(a), vec_max_bits<T>(b)),
                      max(vec_max_bits<T>(c), vec_max_bits<T>(d))));
     }
