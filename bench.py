@@ -74,15 +74,26 @@ def measured_traffic():
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo (what lscpu reads) names it: model name,
+    then family / model / stepping (a virtualized host may report only a
+    generic model name, which the numbers still identify)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" not in line:
+                    if info:
+                        break  # the first processor's block is enough
+                    continue
+                k, v = (t.strip() for t in line.split(":", 1))
+                info.setdefault(k, v)
     except OSError:
         pass
-    import platform
-    return platform.processor() or "unknown"
+    if "model name" not in info:
+        import platform
+        return platform.processor() or "unknown"
+    ids = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+    return f"{info['model name']} ({ids})" if ids else info["model name"]
 
 
 class StreamRef:
