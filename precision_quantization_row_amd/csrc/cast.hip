@@ -1553,17 +1553,27 @@ static int interior_grid() {
   return g;
 }
 
+// The launched grid: at most the resident workgroups, and no more than the
+// work needs, two workgroups per macro tile of an XCD (each takes one 128-row
+// half of a tile when the tiles fit one round), so that a small matrix does
+// not dispatch hundreds of workgroups that find nothing to do. ntx: macro
+// tiles per XCD. Stays a multiple of the XCD count.
+static int64_t fit_grid(int64_t resident, int64_t ntx) {
+  return std::min<int64_t>(resident, (int64_t)IT_XCDS * std::max<int64_t>(1, 2 * ntx));
+}
+
 // General shapes in one launch of the macro-tile kernel (1x16 blocks): every
 // macro tile of the ceil(M / 256) x ceil(K / 256) grid, cut ones included.
 template <typename T, bool ROWW, bool COLW>
 static void launch_cast_general(const CastK& k, hipStream_t s) {
   const int64_t nt = k.n_istrips * k.n_isteps;
-  const int64_t G0 = interior_grid<T, ROWW, COLW, 0, false, true>();
-  const int64_t per = G0 / IT_XCDS, ntx = (nt + IT_XCDS - 1) / IT_XCDS;
+  const int64_t ntx = (nt + IT_XCDS - 1) / IT_XCDS;
+  const int64_t G0 = fit_grid(interior_grid<T, ROWW, COLW, 0, false, true>(), ntx);
+  const int64_t per = G0 / IT_XCDS;
   const int64_t rounds = (ntx + per - 1) / per;
   const bool split = per > 0 && rounds > 0 && 2 * (ntx - (rounds - 1) * per) <= per;
   if (split) {
-    const int64_t G = interior_grid<T, ROWW, COLW, 0, true, true>();
+    const int64_t G = fit_grid(interior_grid<T, ROWW, COLW, 0, true, true>(), ntx);
     hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 0, true, true>), dim3((unsigned)G),
                        dim3(256), 0, s, k);
   } else {
@@ -1577,54 +1587,54 @@ static void launch_cast_kernels(CastK k, const CastArgs& a, hipStream_t s) {
   const dim3 block(256);
   const int64_t ntiles = k.n_istrips * k.n_isteps;
   if (ntiles > 0) {
-    // all resident workgroups: a partly idle last round costs less than
-    // fewer waves per CU. Whether the last round splits its tiles into halves
-    // (at most half as many tiles as an XCD has workgroups) picks the
-    // kernel variant that carries that schedule.
+    // all resident workgroups (a partly idle last round costs less than
+    // fewer waves per CU), unless the tiles need fewer. Whether the last round
+    // splits its tiles into halves (at most half as many tiles as an XCD has
+    // workgroups) picks the kernel variant that carries that schedule.
+    const int64_t ntx = k.n_isteps * ((k.n_istrips + IT_XCDS - 1) / IT_XCDS);
     auto split = [&](int64_t G) {
       const int64_t per = G / IT_XCDS;
-      const int64_t ntx = k.n_isteps * ((k.n_istrips + IT_XCDS - 1) / IT_XCDS);
       const int64_t rounds = (ntx + per - 1) / per;
       return per > 0 && rounds > 0 && 2 * (ntx - (rounds - 1) * per) <= per;
     };
     if (k.grp_G > 0) {
-      if (split(interior_grid<T, ROWW, COLW, 1>())) {
-        const int64_t G = interior_grid<T, ROWW, COLW, 1, true>();
+      if (split(fit_grid(interior_grid<T, ROWW, COLW, 1>(), ntx))) {
+        const int64_t G = fit_grid(interior_grid<T, ROWW, COLW, 1, true>(), ntx);
         hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 1, true>), dim3((unsigned)G),
                            dim3(256), 0, s, k);
       } else {
-        const int64_t G = interior_grid<T, ROWW, COLW, 1>();
+        const int64_t G = fit_grid(interior_grid<T, ROWW, COLW, 1>(), ntx);
         hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 1>), dim3((unsigned)G), dim3(256),
                            0, s, k);
       }
     } else if (k.blk2d) {
-      if (split(interior_grid<T, ROWW, COLW, 2>())) {
-        const int64_t G = interior_grid<T, ROWW, COLW, 2, true>();
+      if (split(fit_grid(interior_grid<T, ROWW, COLW, 2>(), ntx))) {
+        const int64_t G = fit_grid(interior_grid<T, ROWW, COLW, 2, true>(), ntx);
         hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 2, true>), dim3((unsigned)G),
                            dim3(256), 0, s, k);
       } else {
-        const int64_t G = interior_grid<T, ROWW, COLW, 2>();
+        const int64_t G = fit_grid(interior_grid<T, ROWW, COLW, 2>(), ntx);
         hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 2>), dim3((unsigned)G), dim3(256),
                            0, s, k);
       }
     } else if (k.four_six) {
       if constexpr (!(ROWW && COLW)) {
-        if (split(interior_grid<T, ROWW, COLW, 3>())) {
-          const int64_t G = interior_grid<T, ROWW, COLW, 3, true>();
+        if (split(fit_grid(interior_grid<T, ROWW, COLW, 3>(), ntx))) {
+          const int64_t G = fit_grid(interior_grid<T, ROWW, COLW, 3, true>(), ntx);
           hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 3, true>), dim3((unsigned)G),
                              dim3(256), 0, s, k);
         } else {
-          const int64_t G = interior_grid<T, ROWW, COLW, 3>();
+          const int64_t G = fit_grid(interior_grid<T, ROWW, COLW, 3>(), ntx);
           hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 3>), dim3((unsigned)G),
                              dim3(256), 0, s, k);
         }
       }
-    } else if (split(interior_grid<T, ROWW, COLW, 0>())) {
-      const int64_t G = interior_grid<T, ROWW, COLW, 0, true>();
+    } else if (split(fit_grid(interior_grid<T, ROWW, COLW, 0>(), ntx))) {
+      const int64_t G = fit_grid(interior_grid<T, ROWW, COLW, 0, true>(), ntx);
       hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 0, true>), dim3((unsigned)G),
                          dim3(256), 0, s, k);
     } else {
-      const int64_t G = interior_grid<T, ROWW, COLW, 0>();
+      const int64_t G = fit_grid(interior_grid<T, ROWW, COLW, 0>(), ntx);
       hipLaunchKernelGGL((cast_interior_kernel<T, ROWW, COLW, 0>), dim3((unsigned)G), dim3(256), 0,
                          s, k);
     }
