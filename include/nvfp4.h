@@ -152,6 +152,22 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
                              float bound, uint8_t* q_row, uint8_t* s_row, uint8_t* q_col,
                              uint8_t* s_col, const float* noop, void* stream);
 
+/* The whole row-scaled quantize in one call: per-row and per-column amax of
+ * X, then both copies with mode LINE in both directions (row-scaled backward
+ * PR, sequence diagram: the amax pass, then the cast that writes both
+ * copies; fused-amax PR, "Performance": the full quantize is what it times).
+ * Enqueues exactly what nvfp4_amax_rowcol(x, ..., row_amax, col_amax, NULL,
+ * noop, 0, stream) followed by nvfp4_quantize_transpose(x, ..., LINE,
+ * row_amax, LINE, col_amax, bound, q_row, s_row, q_col, s_col, noop, stream)
+ * would, so the results are theirs byte for byte.
+ *   row_amax [M], col_amax [K]: written (the amax vectors)
+ *   q_row, s_row, q_col, s_col: as nvfp4_quantize_transpose, all four required
+ * Validation, noop and errors as those two calls; every argument is checked
+ * before anything is enqueued. */
+int nvfp4_quantize_rowcol(const void* x, int in_dtype, int64_t M, int64_t K, float bound,
+                          float* row_amax, float* col_amax, uint8_t* q_row, uint8_t* s_row,
+                          uint8_t* q_col, uint8_t* s_col, const float* noop, void* stream);
+
 /* Four-over-six block scales (four-over-six grouped-GEMM and backward-
  * overrides PR descriptions: the quantizer is named there together with its
  * MSE choice and its bound-256 second-level scale; nothing more is defined,

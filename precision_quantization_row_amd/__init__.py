@@ -40,7 +40,8 @@ NVFP4_FLAG_FORCE_TWO_KERNEL = 1
 # Every entry point include/nvfp4.h declares.
 EXPORTED = ("nvfp4_amax_path", "nvfp4_amax_rowcol", "nvfp4_group_amax_expand",
             "nvfp4_check_group_end",
-            "nvfp4_quantize_transpose", "nvfp4_quantize_4over6", "nvfp4_quantize_2d",
+            "nvfp4_quantize_transpose", "nvfp4_quantize_rowcol", "nvfp4_quantize_4over6",
+            "nvfp4_quantize_2d",
             "nvfp4_quantize_grouped",
             "nvfp4_quantize_dequantize", "nvfp4_dequantize",
             "nvfp4_status_string")
@@ -82,6 +83,9 @@ def load_library():
     lib.nvfp4_quantize_transpose.argtypes = [vp, c_int, i64, i64, c_int, f32p, c_int, f32p, c_f,
                                              u8p, u8p, u8p, u8p, f32p, vp]
     lib.nvfp4_quantize_4over6.restype = c_int
+    lib.nvfp4_quantize_rowcol.restype = c_int
+    lib.nvfp4_quantize_rowcol.argtypes = [vp, c_int, i64, i64, c_f, f32p, f32p, u8p, u8p, u8p, u8p,
+                                          f32p, vp]
     lib.nvfp4_quantize_4over6.argtypes = [vp, c_int, i64, i64, c_int, f32p, c_int, f32p, c_f,
                                           u8p, u8p, u8p, u8p, f32p, vp]
     lib.nvfp4_quantize_2d.restype = c_int
@@ -223,6 +227,31 @@ def nvfp4_quantize_transpose(x: torch.Tensor, row_mode: int, row_amax: Optional[
                              noop: Optional[torch.Tensor] = None, stream=None) -> None:
     _quantize("nvfp4_quantize_transpose", x, row_mode, row_amax, col_mode, col_amax, bound,
               q_row, s_row, q_col, s_col, noop, stream)
+
+
+def nvfp4_quantize_rowcol(x: torch.Tensor, row_amax: torch.Tensor, col_amax: torch.Tensor,
+                          bound: float, q_row: torch.Tensor, s_row: torch.Tensor,
+                          q_col: torch.Tensor, s_col: torch.Tensor,
+                          noop: Optional[torch.Tensor] = None, stream=None) -> None:
+    """The whole row-scaled quantize in one call: row_amax [M] and col_amax
+    [K] are written, then both copies (mode LINE)."""
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    _dev(x, "x", (torch.bfloat16, torch.float32))
+    M, K = x.shape
+    dev = x.device
+    _dev(row_amax, "row_amax", _F32, M, dev)
+    _dev(col_amax, "col_amax", _F32, K, dev)
+    _dev(q_row, "q_row", (torch.uint8,), M * ((K + 1) // 2), dev)
+    _dev(s_row, "s_row", _SCALE_DTYPES, M * ((K + 15) // 16), dev)
+    _dev(q_col, "q_col", (torch.uint8,), K * ((M + 1) // 2), dev)
+    _dev(s_col, "s_col", _SCALE_DTYPES, K * ((M + 15) // 16), dev)
+    _dev(noop, "noop", _F32, 1, dev)
+    st = lib.nvfp4_quantize_rowcol(_ptr(x), _dtype_code(x), M, K, ctypes.c_float(bound),
+                                   _ptr(row_amax), _ptr(col_amax), _ptr(q_row), _ptr(s_row),
+                                   _ptr(q_col), _ptr(s_col), _ptr(noop), _stream(stream, dev))
+    _check("nvfp4_quantize_rowcol", st)
 
 
 def nvfp4_quantize_4over6(x: torch.Tensor, row_mode: int, row_amax: Optional[torch.Tensor],

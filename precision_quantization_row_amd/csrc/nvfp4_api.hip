@@ -160,6 +160,21 @@ int nvfp4_quantize_transpose(const void* x, int in_dtype, int64_t M, int64_t K, 
                        s_row, q_col, s_col, noop, stream, 0);
 }
 
+int nvfp4_quantize_rowcol(const void* x, int in_dtype, int64_t M, int64_t K, float bound,
+                          float* row_amax, float* col_amax, uint8_t* q_row, uint8_t* s_row,
+                          uint8_t* q_col, uint8_t* s_col, const float* noop, void* stream) {
+  if (x == nullptr || M < 1 || K < 1 || row_amax == nullptr || col_amax == nullptr)
+    return NVFP4_ERR_ARG;
+  if (M > (int64_t)1 << 40 || K > (int64_t)1 << 40) return NVFP4_ERR_ARG;
+  if (in_dtype != NVFP4_BF16 && in_dtype != NVFP4_FP32) return NVFP4_ERR_ARG;
+  if (!valid_bound(bound)) return NVFP4_ERR_ARG;
+  if (!q_row || !s_row || !q_col || !s_col) return NVFP4_ERR_ARG;
+  const int rc = nvfp4_amax_rowcol(x, in_dtype, M, K, row_amax, col_amax, nullptr, noop, 0, stream);
+  if (rc != NVFP4_OK) return rc;
+  return quantize_impl(x, in_dtype, M, K, NVFP4_AMAX_LINE, row_amax, NVFP4_AMAX_LINE, col_amax,
+                       bound, q_row, s_row, q_col, s_col, noop, stream, 0);
+}
+
 int nvfp4_quantize_4over6(const void* x, int in_dtype, int64_t M, int64_t K, int row_mode,
                           const float* row_amax, int col_mode, const float* col_amax, float bound,
                           uint8_t* q_row, uint8_t* s_row, uint8_t* q_col, uint8_t* s_col,
