@@ -45,3 +45,19 @@ def test_step_bytes_of_the_headline_workload():
     # once, both copies of codes and scales written once
     want = 2 * M * K * 2 + 2 * 4 * (M + K) + M * K // 2 + M * K // 16 + K * M // 2 + K * M // 16
     assert workloads.algorithmic_bytes(M, K, 2) == want
+
+
+def test_cases_are_named_and_selectable():
+    """Every group of other rows is a named case; --case accepts exactly those
+    names (and rejects others before touching a GPU)."""
+    b = _bench()
+    assert set(b.CASES) == {"amax", "2d", "4over6", "qdq", "fp32_edge", "grouped", "small"}
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--case", "nope"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "invalid choice" in r.stderr
+
+
+def test_cpu_model_names_the_host():
+    b = _bench()
+    m = b.cpu_model()
+    assert isinstance(m, str) and m and m != "unknown"
