@@ -9,7 +9,9 @@ The input is resident in HBM before timing starts. value = algorithmic bytes
 of the step (X read twice, amax vectors written and read once, all codes and
 scales written once) / step time, in GB/s.
 
-The headline region holds K whole steps with HIP events only at its two ends.
+The headline region holds K whole steps with HIP events only at its two ends,
+queued right after 50 untimed steps (so that a short region does not start on
+a GPU still ramping up from an idle wait).
 The roofline figure is the cast kernel's duration where it runs in the step:
 a second region of K steps records an event pair around each cast (after its
 amax pass), and the pairs' average gives the roofline fraction (algorithmic
@@ -46,6 +48,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published peak
+# Untimed steps (about 10 ms of the same work) queued right before each
+# headline region: after an idle wait the GPU needs about that long to reach
+# its steady clock. The first 20-step region of a fresh process read 206-215 us
+# per step with 0-20 such steps and 200.5-202.5 us with 50 (same GPU).
+RUN_IN = 50
 METRIC = "row-scaled NVFP4 quantize-transpose GB/s (in+out) and % of HBM peak, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cast_llm_mlp_traffic.json")
 
@@ -269,10 +276,13 @@ def case_2d(c):
     # region pays a fixed cost where it starts), then the same steps with an
     # event pair around each cast
     n = 200
-    step_ms = c.timed(lambda i: (amax(i), f2d(i)), n, 2)
+    step_ms = c.timed(lambda i: (amax(i), f2d(i)), n, 2, lead=RUN_IN)
     ev = c.events(n)
     torch.cuda.synchronize()
-    c.hold(4 * n)
+    c.hold(4 * n + 2 * RUN_IN)
+    for i in range(RUN_IN):
+        amax(i)
+        f2d(i)
     for i in range(n):
         amax(i)
         ev[i][0].record()
@@ -556,14 +566,20 @@ def main():
         ms = args.hold_ms if args.hold_ms is not None else 1.0 + 1.5 * n_calls * host_ms_per_call[0]
         torch.cuda._sleep(int(ms * sleep_cycles_per_ms))
 
-    def timed(fn, n, calls_per_fn=1):
+    def timed(fn, n, calls_per_fn=1, lead=0):
         """Average time of fn(0..n-1) launched back to back, HIP events on the
         launch stream at the two ends of the region only (an event between two
-        kernels would add a gap of its own)."""
+        kernels would add a gap of its own). lead: untimed launches of fn
+        queued between the spin kernel and the first event, so that the timed
+        region starts on a GPU that is already running the same work (a
+        region that starts right after the idle wait can read a few percent
+        slower when it is short)."""
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        hold_queue(n * calls_per_fn)
+        hold_queue((n + lead) * calls_per_fn)
+        for i in range(lead):
+            fn(i)
         e0.record()
         for i in range(n):
             fn(i)
@@ -595,14 +611,17 @@ def main():
 
     K_steps = args.steps
     step_bytes = workloads.algorithmic_bytes(M, K, 2)
-    # headline: K whole steps
-    ms_per_step = timed(lambda i: (amax(i), cast(i)), K_steps, 2)
+    # headline: K whole steps (after RUN_IN untimed ones in the same queue)
+    ms_per_step = timed(lambda i: (amax(i), cast(i)), K_steps, 2, lead=RUN_IN)
     # per-kernel regions: the same launches, one kind at a time
     # the cast inside the step: an event pair around each cast, after its amax
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K_steps)]
     torch.cuda.synchronize()
-    hold_queue(4 * K_steps)
+    hold_queue(4 * K_steps + 2 * RUN_IN)
+    for i in range(RUN_IN):
+        amax(i)
+        cast(i)
     for i in range(K_steps):
         amax(i)
         ev[i][0].record()
@@ -610,8 +629,8 @@ def main():
         ev[i][1].record()
     torch.cuda.synchronize()
     cast_step = sum(a.elapsed_time(b) for a, b in ev) / K_steps
-    cast_avg = timed(cast, K_steps)
-    amax_avg = timed(amax, K_steps)
+    cast_avg = timed(cast, K_steps, lead=RUN_IN)
+    amax_avg = timed(amax, K_steps, lead=RUN_IN)
     cast_bytes = M * K * 2 + 4 * (M + K) + (M * ((K + 1) // 2) + M * ((K + 15) // 16)
                                             + K * ((M + 1) // 2) + K * ((M + 15) // 16))
     amax_bytes = M * K * 2 + 4 * (M + K)
