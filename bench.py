@@ -120,7 +120,8 @@ class StreamRef:
         vp, i64, c_int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         for name, args in (("stream_read", [vp, i64, vp, c_int, c_int, vp]),
                            ("stream_write", [vp, i64, c_int, vp]),
-                           ("stream_copy", [vp, vp, i64, c_int, vp])):
+                           ("stream_copy", [vp, vp, i64, c_int, vp]),
+                           ("stream_pieces", [vp, i64, c_int, c_int, c_int, vp])):
             fn = getattr(lib, name)
             fn.restype = c_int
             fn.argtypes = args
@@ -142,6 +143,11 @@ class StreamRef:
     def copy(self, a, b, grid=4096):
         assert self.lib.stream_copy(a.data_ptr(), b.data_ptr(), a.numel() * a.element_size(), grid,
                                     self._st()) == 0
+
+    def pieces(self, t, piece, nt, grid=4096):
+        """Write t in `piece`-byte pieces of scattered 128-byte lines."""
+        assert self.lib.stream_pieces(t.data_ptr(), t.numel() * t.element_size(), piece, int(nt),
+                                      grid, self._st()) == 0
 
     def flush(self):
         """Read 512 MB (twice the memory-side cache) with ordinary, caching
@@ -454,8 +460,59 @@ def case_small(c):
     return res
 
 
+def case_hw(c):
+    """The write-path probes (bench_ref/stream_ref.hip), not part of the
+    default line: 117 MB (the size of one copy's codes at 8192 x 28672)
+    written as scattered pieces of 128, 64, 32 or 16 bytes per 128-byte line,
+    with non-temporal or ordinary stores, each write followed by a 470 MB
+    non-temporal read (the size of X), which absorbs the write-back of the
+    lines the write left dirty in the memory-side cache. Medians of 10
+    repetitions, an event pair around each kernel; each repetition starts
+    after a read of its own, so no dirty line is left from the one before."""
+    torch, ref, dev = c.torch, c.ref, c.dev
+    nw, nr = 117440512, 469762048
+    wbuf = torch.empty(nw, dtype=torch.uint8, device=dev)
+    rbuf = torch.ones(nr, dtype=torch.uint8, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def med(v):
+        v = sorted(v)
+        return 0.5 * (v[(len(v) - 1) // 2] + v[len(v) // 2])
+
+    def pair(write):
+        tw, tr = [], []
+        for _ in range(10):
+            ref.read(rbuf)
+            torch.cuda.synchronize()
+            e0, e1, e2 = ev(), ev(), ev()
+            c.hold(3)
+            e0.record()
+            write()
+            e1.record()
+            ref.read(rbuf)
+            e2.record()
+            torch.cuda.synchronize()
+            tw.append(e0.elapsed_time(e1) * 1e3)
+            tr.append(e1.elapsed_time(e2) * 1e3)
+        return med(tw), med(tr)
+
+    res = {}
+    _, r0 = pair(lambda: ref.read(wbuf))  # a read in place of the write: the read alone
+    res["read_470MB_after_a_read"] = {"us": round(r0, 2)}
+    for piece in (128, 64, 32, 16):
+        for nt in (True, False):
+            w_us, r_us = pair(lambda: ref.pieces(wbuf, piece, nt))
+            res[f"write_117MB_{piece}B_pieces_{'nt' if nt else 'cached'}"] = {
+                "write_us": round(w_us, 2), "read_470MB_after_us": round(r_us, 2),
+                "sum_us": round(w_us + r_us, 2),
+                "write_plus_drain_us": round(w_us + r_us - r0, 2)}
+    return res
+
+
 CASES = {"amax": case_amax, "2d": case_2d, "4over6": case_4over6, "qdq": case_qdq,
-         "fp32_edge": case_fp32_edge, "grouped": case_grouped, "small": case_small}
+         "fp32_edge": case_fp32_edge, "grouped": case_grouped, "small": case_small,
+         "hw": case_hw}
+DEFAULT_CASES = ("amax", "2d", "4over6", "qdq", "fp32_edge", "grouped", "small")
 
 
 def other_rows(ctx, names=None):
@@ -463,7 +520,7 @@ def other_rows(ctx, names=None):
     Back-to-back regions have events at their ends only; bytes are those each
     launch actually has to move (the two-kernel amax reads X twice)."""
     res = {}
-    for name in (names or CASES):
+    for name in (names or DEFAULT_CASES):
         res.update(CASES[name](ctx))
     return res
 

@@ -1,7 +1,8 @@
 // stream_ref.hip -- reference streaming kernels for measuring what this GPU's
 // HBM sustains (the achievable ceiling printed next to the quantize path's
 // bandwidth). Not part of the NVFP4 library: plain 16-byte non-temporal reads,
-// writes and copies over a buffer, grid-stride, with nothing else per byte.
+// writes and copies over a buffer, grid-stride, with nothing else per byte,
+// and a writer of scattered partial lines (the store-pattern probe).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -80,6 +81,31 @@ __global__ void __launch_bounds__(kThreads) copy_kernel(const u32x4* __restrict_
   }
 }
 
+// Writes a buffer of `lines` 128-byte lines in pieces of `piece` bytes (16,
+// 32, 64 or 128), one 16-byte store per thread and step. Consecutive threads
+// fill a piece (piece / 16 of them), and the next group of threads writes the
+// same part of the next line: piece q goes to line q % lines at offset
+// (q / lines) * piece. So one wave instruction writes 64 * 16 / piece pieces
+// in as many consecutive lines (piece 128: 1 KB of whole lines), and a line's
+// other pieces come from instructions much later -- the pattern of scattered
+// partial lines. NT: non-temporal stores; otherwise ordinary ones.
+template <bool NT>
+__global__ void __launch_bounds__(kThreads) piece_write_kernel(u32x4* __restrict__ y, int64_t lines,
+                                                               int piece, uint32_t v) {
+  const int per = piece / 16;  // threads (16-byte stores) per piece
+  const int64_t units = lines * 8;
+  const u32x4 w = {v, v, v, v};
+  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < units;
+       u += (int64_t)gridDim.x * kThreads) {
+    const int64_t q = u / per;
+    const int k = (int)(u - q * per);
+    const int64_t line = q % lines, part = q / lines;
+    u32x4* d = y + line * 8 + part * per + k;
+    if constexpr (NT) __builtin_nontemporal_store(w, d);
+    else *d = w;
+  }
+}
+
 bool ok(const void* p, int64_t bytes) {
   return p != nullptr && bytes > 0 && bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 }
@@ -120,6 +146,24 @@ int stream_copy(const void* x, void* y, int64_t bytes, int grid, void* stream) {
   hipLaunchKernelGGL(copy_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(x),
                      static_cast<u32x4*>(y), bytes / 16);
+  return done();
+}
+
+// bytes: a positive multiple of 128; piece: 16, 32, 64 or 128; nt != 0:
+// non-temporal stores. -1 for a bad argument, else 0 or -3 after enqueuing
+// one kernel of `grid` workgroups on `stream`.
+int stream_pieces(void* y, int64_t bytes, int piece, int nt, int grid, void* stream) {
+  if (!ok(y, bytes) || bytes % 128 != 0 || grid < 1 ||
+      (piece != 16 && piece != 32 && piece != 64 && piece != 128))
+    return -1;
+  if (nt)
+    hipLaunchKernelGGL(piece_write_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<u32x4*>(y), bytes / 128, piece,
+                       0u);
+  else
+    hipLaunchKernelGGL(piece_write_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<u32x4*>(y), bytes / 128, piece,
+                       0u);
   return done();
 }
 

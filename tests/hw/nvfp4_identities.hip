@@ -98,6 +98,16 @@ __global__ void div6_kernel(uint32_t start, int64_t n, float* out_rn, float* out
   }
 }
 
+// The scaled FP4 converter with an arbitrary scale operand: element i is
+// converted with scale s[i] (the pair's second value is 0); byte i receives
+// the pair's code byte (element i in the low nibble).
+__global__ void fp4_scaled_kernel(const float* x, const float* s, int64_t n, uint8_t* out) {
+  for (int64_t t = gtid(); t < n; t += gstride()) {
+    const uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[t], 0.0f, s[t], 0);
+    out[t] = (uint8_t)(w & 0xFFu);
+  }
+}
+
 unsigned grid_for(int64_t n) {
   const int64_t g = (n + kThreads - 1) / kThreads;
   return (unsigned)(g < 1 ? 1 : (g > 65536 ? 65536 : g));
@@ -123,6 +133,7 @@ extern "C" {
 //   probe_bf16        out_hw [n / 2] dwords, out_sw [n] halfwords
 //   probe_recip       out_rn [n], out_newton [n] floats
 //   probe_div6        out_rn [n], out_tt [n] floats
+//   probe_fp4_scaled  x [n], s [n] floats in; out [n] bytes
 int probe_fp4_encode(uint32_t start, int64_t n, void* out, void* stream) {
   if (!run_ok(start, n, 8) || out == nullptr) return -1;
   hipLaunchKernelGGL(fp4_encode_kernel, dim3(grid_for(n / 8)), dim3(kThreads), 0,
@@ -167,6 +178,14 @@ int probe_div6(uint32_t start, int64_t n, void* out_rn, void* out_tt, void* stre
   hipLaunchKernelGGL(div6_kernel, dim3(grid_for(n)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), start, n, static_cast<float*>(out_rn),
                      static_cast<float*>(out_tt));
+  return done();
+}
+
+int probe_fp4_scaled(const void* x, const void* s, int64_t n, void* out, void* stream) {
+  if (x == nullptr || s == nullptr || out == nullptr || n <= 0) return -1;
+  hipLaunchKernelGGL(fp4_scaled_kernel, dim3(grid_for(n)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const float*>(x),
+                     static_cast<const float*>(s), n, static_cast<uint8_t*>(out));
   return done();
 }
 

@@ -51,7 +51,8 @@ def test_cases_are_named_and_selectable():
     """Every group of other rows is a named case; --case accepts exactly those
     names (and rejects others before touching a GPU)."""
     b = _bench()
-    assert set(b.CASES) == {"amax", "2d", "4over6", "qdq", "fp32_edge", "grouped", "small"}
+    assert set(b.CASES) == {"amax", "2d", "4over6", "qdq", "fp32_edge", "grouped", "small", "hw"}
+    assert set(b.DEFAULT_CASES) == set(b.CASES) - {"hw"}
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--case", "nope"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "invalid choice" in r.stderr

@@ -19,7 +19,11 @@ the CPU oracle on the host, and a test stops at the first run that differs:
 * recip_rn: every positive finite D, against min(RN(1/D), FLT_MAX); the bare
   Newton form recip_newton wherever the kernels use it (recip_fast_ok);
 * div6_rn: every finite x >= 0, and the two-term div6_two_term for
-  x >= 2^-121, against RN(x / 6)."""
+  x >= 2^-121, against RN(x / 6);
+* the scaled form of the E2M1 converter with arbitrary scales s: it encodes
+  x / 2^floor(log2 s), so it takes the scale's exponent only and cannot fold
+  a block's encode factor into the conversion (the kernels multiply first and
+  convert with scale 1)."""
 from __future__ import annotations
 
 import ctypes
@@ -54,7 +58,8 @@ def _probes():
                            ("probe_decode", [vp, vp, vp, vp, vp]),
                            ("probe_bf16", [u32, i64, vp, vp, vp]),
                            ("probe_recip", [u32, i64, vp, vp, vp]),
-                           ("probe_div6", [u32, i64, vp, vp, vp])):
+                           ("probe_div6", [u32, i64, vp, vp, vp]),
+                           ("probe_fp4_scaled", [vp, vp, i64, vp, vp])):
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = args
@@ -190,3 +195,30 @@ def test_div6_every_magnitude():
         pat = np.arange(start, start + n, dtype=np.uint32)
         _same("div6_two_term (x >= 2^-121)", start, tt[:n].cpu().numpy().view(np.uint32), want,
               pat >= 0x03000000)
+
+
+def test_scaled_fp4_converter_takes_only_the_scale_exponent():
+    lib = _probes()
+    g = np.random.RandomState(12)
+    n = 1 << 20
+    e = g.randint(-20, 21, n)
+    m = np.where(g.rand(n) < 0.1, 1.0, 1.0 + g.rand(n))  # mostly not a power of two
+    s = (m * np.exp2(e)).astype(np.float32)
+    # random magnitudes around the E2M1 range, and values at and beside its
+    # rounding ties, all relative to 2^e
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    t = np.where(g.rand(n) < 0.5, g.randn(n) * 3.0,
+                 ties[g.randint(0, len(ties), n)] * (1.0 + g.choice([-1e-6, 0.0, 1e-6], n))
+                 * np.where(g.rand(n) < 0.5, -1.0, 1.0))
+    x = (t * np.exp2(e)).astype(np.float32)
+    xd = torch.from_numpy(x).to(DEV)
+    sd = torch.from_numpy(s).to(DEV)
+    out = torch.empty(n, dtype=torch.uint8, device=DEV)
+    say("[gpu] identities: scaled E2M1 converter over 2^20 random (x, s)")
+    assert lib.probe_fp4_scaled(_ptr(xd), _ptr(sd), n, _ptr(out), _stream()) == 0
+    hw = out.cpu().numpy() & 0xF
+    scaled = (x / np.exp2(e).astype(np.float32)).astype(np.float32)  # exact: a power of two
+    _same("cvt_scalef32_pk_fp4_f32 vs E2M1(x / 2^floor(log2 s))", 0, hw, oracle.e2m1_encode(scaled))
+    # a plain division by s gives other codes on a good part of these inputs
+    by_s = oracle.e2m1_encode((x / s).astype(np.float32))
+    assert float((hw != by_s).mean()) > 0.05
